@@ -1,0 +1,181 @@
+/*
+ * moe_mx4.h — C ABI of the routed MXFP4 mixture-of-experts chain for MI355X (gfx950).
+ *
+ * The chain (gpt-oss routed experts) runs as five stream-ordered calls:
+ *
+ *   moe_route_topk  logits -> top-k expert ids + routing weights
+ *   moe_bucket      ids    -> CSR of routed rows per expert with padded prefix bases
+ *   mx4_moe_gemv    gate_up / down MXFP4 projection, few rows per expert (decode)
+ *   mx4_moe_gemm    the same function on MFMA, many rows per expert (prefill)
+ *   moe_combine     router-weighted sum of each token's expert rows, in slot order
+ *
+ * Sources (web pages on the daScript repository's dasLLAMA engine; cited by tag below):
+ *   [fusion]  PR #3579 "dasLLAMA gpt-oss arc", commit log, the Metal fusion-lane commit: the
+ *             bucket pass computes each expert's padded-prefix base inside its workgroup and
+ *             publishes it (the separate prefix pass is gone, the CSR is unchanged bit for bit);
+ *             the expert matmul starts its accumulators from the expert's bias row; the prefill
+ *             SwiGLU-OAI skips ghost rows beyond the last bucket's padded end.
+ *   [chain]   PR #3579, commit log, the fused MoE expert chain commit, and the PR body's section
+ *             "Fused MoE expert chain": stage 0 = gate and up rows + bias + activation, stage 1 =
+ *             down rows + bias, then the routing-weighted sum taken in slot order.
+ *   [mx4]     PR #3558 "dasLLAMA: dig the last two board reds green", section "gpt-oss: mx4
+ *             kernels to the lab-winning shape" and its ladder table: MXFP4 weights decoded via
+ *             a 16-entry e2m1 table and one e8m0 exponent byte per 32-value block, bit-exact for
+ *             every one of the 256 exponent bytes; gpt-oss shapes E=32, nfe=dim=2880, k=4.
+ *
+ * Conventions shared by every call
+ *   - All pointers other than the `mx4_experts` descriptor itself are DEVICE pointers owned by
+ *     the caller. The library never allocates or frees device memory and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues work on it and
+ *     returns; nothing synchronizes. Buffers must stay alive until the stream reaches the work.
+ *   - Arguments are validated on the host before anything is enqueued; on any error nothing is
+ *     enqueued and the status says why. Data preconditions (finite logits, ids in [0,E), a CSR
+ *     produced by moe_bucket with the same E/tile_m/mpad_max) are documented, not checked.
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   - Results are deterministic: two identical calls produce bit-identical outputs (no float
+ *     atomics anywhere).
+ */
+#ifndef MOE_MX4_H
+#define MOE_MX4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,  /* NULL pointer, non-positive size, k outside [1, min(E, MOE_MAX_K)]          */
+  MOE_ESHAPE = 2,  /* K % 32 != 0, odd N with SwiGLU, tile_m outside [1, MOE_MAX_TILE_M],
+                      mpad_max smaller than moe_mpad_max(...), E above MOE_MAX_E            */
+  MOE_EALIGN = 3,  /* weight nibble plane not 16-byte aligned, activations/outputs not 4-byte  */
+  MOE_ELAUNCH = 4  /* the HIP runtime reported an error when the kernel was enqueued          */
+} moe_status;
+
+typedef enum {
+  MOE_ACT_NONE = 0,       /* out = f32 [mpad_max][N]: bias + a . W^T                              */
+  MOE_ACT_SWIGLU_OAI = 1  /* out = bf16 [mpad_max][N/2]: clamped SwiGLU-OAI of (gate, up) halves */
+} moe_act;
+
+#define MOE_MAX_K 16        /* experts per token */
+#define MOE_MAX_E 1024      /* experts per layer */
+#define MOE_MAX_TILE_M 256  /* bucket padding granule */
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* moe_strerror(int status);
+
+/*
+ * Row capacity of the CSR for T tokens routed to k of E experts with padding granule tile_m:
+ *   R = T*k routed rows; every non-empty expert pads its rows up to a multiple of tile_m, so at
+ *   most min(E, R) experts each add at most tile_m-1 padding rows:
+ *   mpad_max = roundup(R + min(E, R) * (tile_m - 1), tile_m).
+ * Returns -1 for invalid arguments (T < 1, k < 1, E < 1, k > E, tile_m < 1). Host-only.
+ */
+int64_t moe_mpad_max(int64_t T, int k, int E, int tile_m);
+
+/*
+ * Top-k routing ([chain]: expert ids per token; [mx4]: k = 4 experts per token at gpt-oss shape).
+ *   logits  f32 [T][E], row-major, finite.
+ *   ids     i32 [T][k] out: for each token, the k largest logits in descending order; equal logits
+ *           are ordered by ascending expert id (-0.0 and +0.0 are equal).
+ *   w       f32 [T][k] out: softmax over the k selected logits,
+ *           w[s] = exp(l[s]-l[0]) / sum_j exp(l[j]-l[0]), evaluated in double and rounded to f32.
+ * Errors: MOE_EINVAL for NULL pointers, T < 1, E < 1, k < 1, k > min(E, MOE_MAX_K);
+ *         MOE_ESHAPE for E > MOE_MAX_E.
+ */
+int moe_route_topk(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w,
+                   void* stream);
+
+/*
+ * Bucket / CSR of routed rows per expert with padded prefix bases ([fusion]: one workgroup per
+ * expert computes its own padded-prefix base and publishes basep[e]).
+ *   ids      i32 [T][k] in, each id in [0, E), distinct within a token.
+ *   counts   i32 [E]   out: cnt[e] = number of (t, s) with ids[t][s] == e.
+ *   basep    i32 [E+1] out: basep[0] = 0, basep[e+1] = basep[e] + roundup(cnt[e], tile_m).
+ *   row_tok  i32 [mpad_max] out: row basep[e] + j holds the token of expert e's j-th routed row,
+ *            rows ordered by ascending token; padding rows [basep[e]+cnt[e], basep[e+1]) and ghost
+ *            rows [basep[E], mpad_max) hold -1.
+ *   pos      i32 [T][k] out: the CSR row of (t, s), i.e. row_tok[pos[t][s]] == t.
+ * Errors: MOE_EINVAL for NULL pointers, T < 1, k < 1, E < 1, k > min(E, MOE_MAX_K);
+ *         MOE_ESHAPE for tile_m outside [1, MOE_MAX_TILE_M], E > MOE_MAX_E, or
+ *         mpad_max < moe_mpad_max(T, k, E, tile_m).
+ */
+int moe_bucket(const int32_t* ids, int64_t T, int k, int E, int tile_m, int64_t mpad_max,
+               int32_t* counts, int32_t* basep, int32_t* row_tok, int32_t* pos, void* stream);
+
+/*
+ * A stack of E MXFP4 expert matrices W[e] of N rows by K columns ([mx4]).
+ *   q     u8 [E][N][K/2]: e2m1 codes, two per byte; element 2i of a row is the LOW nibble of byte
+ *         i, element 2i+1 the HIGH nibble. 16-byte aligned (every 32-element block is 16 bytes).
+ *   s     u8 [E][N][K/32]: e8m0 exponent byte of each 32-element block.
+ *   bias  f32 [E][N], or NULL for no bias.
+ * Decoded element = e2m1(code) * 2^(s - 127) as an fp32 value (+-inf if it exceeds the fp32
+ * range; NaN for s == 255), where e2m1 = {0, .5, 1, 1.5, 2, 3, 4, 6} with bit 3 the sign.
+ * For the gate_up projection N = 2*ffn, rows [0, ffn) are the gate and rows [ffn, 2*ffn) the up
+ * projection; for the down projection N = dim.
+ * The descriptor itself is a HOST struct; q, s and bias are device pointers.
+ */
+typedef struct {
+  const uint8_t* q;
+  const uint8_t* s;
+  const float* bias;
+  int E;
+  int N;
+  int K;
+} mx4_experts;
+
+/*
+ * Routed-expert MXFP4 projection, bias-seeded, with an optional fused SwiGLU-OAI epilogue
+ * ([fusion]: accumulators start from the expert's bias row, the SwiGLU-OAI epilogue skips ghost
+ * rows; [chain]: gate and up rows + bias + activation in one stage).
+ * For every expert e and every live CSR row r in [basep[e], basep[e] + counts[e]):
+ *   act row   x = a[a_row[r]] if a_row != NULL, else a[r]          (bf16, K elements)
+ *   g[n]      = bias[e][n] + sum_i x[i] * W[e][n][i]   (fp32 accumulation), n in [0, N)
+ *   MOE_ACT_NONE:        out f32  [mpad_max][N]:   out[r][n] = g[n]
+ *   MOE_ACT_SWIGLU_OAI:  out bf16 [mpad_max][N/2]: with F = N/2, for j in [0, F):
+ *        gc = min(g[j], limit), uc = clamp(g[F+j], -limit, limit),
+ *        out[r][j] = bf16_rne( gc * sigmoid(alpha * gc) * (uc + 1) )
+ * Rows that are padding or ghost (not live) are left UNWRITTEN; empty experts do no work.
+ *   a         bf16 [a_rows][K] activations, row-major.
+ *   a_row     i32 [mpad_max] or NULL (the row_tok array of moe_bucket for the gate_up step;
+ *             NULL for the down step, whose input rows are already in CSR order). Every live
+ *             row's a_row entry must be in [0, a_rows); with a_row == NULL a_rows >= mpad_max.
+ *   counts, basep: from moe_bucket (same E, tile_m, mpad_max).
+ * mx4_moe_gemv and mx4_moe_gemm compute the same function with different kernels: the GEMV
+ * streams each weight byte once through the VALU (decode, a handful of rows per expert), the
+ * GEMM dequantizes MXFP4 to bf16 in registers and runs bf16 MFMA with fp32 accumulation
+ * (prefill, tens to hundreds of rows per expert). Their results agree within fp32 summation
+ * order, not bit-for-bit.
+ * Errors: MOE_EINVAL for NULL a/w/q/s/counts/basep/out, a_rows < 1, E/N < 1, mpad_max < 1,
+ *         unknown act; MOE_ESHAPE for K < 32 or K % 32 != 0, odd N with MOE_ACT_SWIGLU_OAI,
+ *         tile_m outside [1, MOE_MAX_TILE_M], E > MOE_MAX_E, a_row == NULL with
+ *         a_rows < mpad_max; MOE_EALIGN for q not 16-byte aligned or a/out not 4-byte aligned;
+ *         MOE_ELAUNCH if the runtime rejects the launch.
+ */
+int mx4_moe_gemv(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const mx4_experts* w,
+                 const int32_t* counts, const int32_t* basep, int tile_m, int64_t mpad_max,
+                 int act, float alpha, float limit, void* out, void* stream);
+
+int mx4_moe_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const mx4_experts* w,
+                 const int32_t* counts, const int32_t* basep, int tile_m, int64_t mpad_max,
+                 int act, float alpha, float limit, void* out, void* stream);
+
+/*
+ * Router-weighted combine ([chain]: routing-weighted sum of the expert rows in slot order).
+ *   y[t][n] = sum_{s=0..k-1} w[t][s] * d[pos[t][s]][n], accumulated in fp32 in slot order.
+ *   d    f32 [d_rows][D], the down projection's output in CSR row order (bias included).
+ *   pos  i32 [T][k] from moe_bucket; every entry in [0, d_rows).
+ *   w    f32 [T][k] from moe_route_topk.
+ *   y    f32 [T][D] out, fully written.
+ * Errors: MOE_EINVAL for NULL pointers, T < 1, k < 1 or k > MOE_MAX_K, D < 1, d_rows < 1;
+ *         MOE_EALIGN for d or y not 4-byte aligned.
+ */
+int moe_combine(const float* d, int64_t d_rows, const int32_t* pos, const float* w, int64_t T,
+                int k, int D, float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MX4_H */

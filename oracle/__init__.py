@@ -1,0 +1,12 @@
+"""CPU oracle of the routed MXFP4 expert chain — test infrastructure only.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import this package.
+It shares no code with the HIP library and never imports it.
+"""
+from .mx4_oracle import (E2M1_TABLE, bf16_round, bf16_to_f64, bucket, chain, combine, dequant,
+                         e2m1_decode, e8m0_decode, live_rows, mpad_max, project, project_at,
+                         route_topk, swiglu_oai, unpack_codes)
+
+__all__ = ["E2M1_TABLE", "bf16_round", "bf16_to_f64", "bucket", "chain", "combine", "dequant",
+           "e2m1_decode", "e8m0_decode", "live_rows", "mpad_max", "project", "project_at",
+           "route_topk", "swiglu_oai", "unpack_codes"]

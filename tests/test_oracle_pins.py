@@ -1,0 +1,411 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each test checks one oracle function against something the oracle does not compute itself: the
+bit-field definition of the MX formats, exact rational arithmetic, brute force on tiny inputs,
+invariants of the CSR, or a library routine. The comment on each test names the mistake it
+catches. No GPU is needed.
+"""
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp4_mixture_experts_route_amd import synth
+
+FLT_MAX = float(np.finfo(np.float32).max)
+ALPHA, LIMIT = synth.ALPHA, synth.LIMIT
+
+
+# ---------------------------------------------------------------------------------------------
+# independent decoders, written from the bit-field definitions (OCP MX v1.0)
+# ---------------------------------------------------------------------------------------------
+
+def e2m1_bits(code):
+    """(sign, magnitude) of an FP4 E2M1 code from its bit fields: bit 3 sign, bits 2..1 exponent
+    with bias 1, bit 0 mantissa; exponent field 0 is subnormal (0.m * 2^0)."""
+    sign = -1 if (code >> 3) & 1 else 1
+    ex, man = (code >> 1) & 3, code & 1
+    mag = Fraction(man, 2) if ex == 0 else Fraction(2) ** (ex - 1) * (1 + Fraction(man, 2))
+    return sign, mag
+
+
+def element_code(row_bytes, i):
+    """Code of element i of a packed row, by the byte/nibble rule stated in the C header."""
+    byte = int(row_bytes[i // 2])
+    return byte & 0xF if i % 2 == 0 else byte >> 4
+
+
+def bf16_fraction(bits):
+    return Fraction(float(oracle.bf16_to_f64(np.uint16(bits))))
+
+
+# ---------------------------------------------------------------------------------------------
+# MX decode
+# ---------------------------------------------------------------------------------------------
+
+def test_e2m1_all_16_codes_match_bit_fields():
+    # catches a wrong table entry, a sign error, or +0 for code 8
+    for c in range(16):
+        sign, mag = e2m1_bits(c)
+        v = float(oracle.e2m1_decode(c))
+        assert Fraction(abs(v)) == mag, c
+        assert math.copysign(1.0, v) == sign, c
+
+
+def test_e8m0_all_256_bytes():
+    # catches an off-by-one bias, flushing of the 2^-127 subnormal, or a finite byte 255
+    for e in range(256):
+        v = float(oracle.e8m0_decode(e))
+        if e == 255:
+            assert math.isnan(v)
+        else:
+            assert Fraction(v) == Fraction(2) ** (e - 127), e
+
+
+def test_dequant_every_code_with_every_scale():
+    # 16 codes x 256 scale bytes: exact fp32 value, +-inf past FLT_MAX, NaN for byte 255
+    q = np.array([[c | (c << 4)] * 16 for c in range(16)], dtype=np.uint8)      # [16 rows][16 B]
+    for e in range(256):
+        W = oracle.dequant(q, np.full((16, 1), e, dtype=np.uint8))              # [16][32]
+        assert W.dtype == np.float32 and W.shape == (16, 32)
+        for c in range(16):
+            sign, mag = e2m1_bits(c)
+            for v in W[c]:
+                v = float(v)
+                if e == 255:
+                    assert math.isnan(v)
+                    continue
+                exact = mag * Fraction(2) ** (e - 127)
+                if exact > FLT_MAX:
+                    assert math.isinf(v) and math.copysign(1.0, v) == sign
+                else:
+                    assert Fraction(abs(v)) == exact and math.copysign(1.0, v) == sign, (c, e)
+
+
+def test_nibble_order_low_nibble_is_even_element():
+    # catches swapped nibbles: byte 0x21 holds element 0 = code 1 (0.5), element 1 = code 2 (1.0)
+    q = np.zeros((1, 16), dtype=np.uint8)
+    q[0, 0] = 0x21
+    q[0, 15] = 0xF7          # element 30 = code 7 (6.0), element 31 = code 15 (-6.0)
+    W = oracle.dequant(q, np.array([[127]], dtype=np.uint8))[0]
+    assert W[0] == 0.5 and W[1] == 1.0 and W[30] == 6.0 and W[31] == -6.0
+    assert np.all(W[2:30] == 0)
+
+
+def test_scale_applies_to_its_own_32_block():
+    # catches a scale indexed per element or per row: block 1 uses scale byte 1
+    q = np.full((1, 32), 0x22, dtype=np.uint8)           # every element code 2 = 1.0
+    W = oracle.dequant(q, np.array([[127, 129]], dtype=np.uint8))[0]
+    assert np.all(W[:32] == 1.0) and np.all(W[32:] == 4.0)
+
+
+# ---------------------------------------------------------------------------------------------
+# bf16 rounding
+# ---------------------------------------------------------------------------------------------
+
+def test_bf16_round_matches_torch_conversion():
+    # torch's float32 -> bfloat16 conversion is round-to-nearest-even; on values that are exact
+    # float32, the oracle's float64 rounding must agree bit for bit (ties, subnormals, overflow)
+    g = np.random.default_rng(5)
+    v = np.concatenate([
+        g.standard_normal(20000).astype(np.float32) * 100,
+        (g.standard_normal(2000) * 1e-39).astype(np.float32),                  # subnormals
+        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3.3961e38, 3.39e38, -3.4e38,
+                  2 ** -133, 2 ** -134, 3 * 2 ** -134, 0.0, -0.0], dtype=np.float32),
+        (g.integers(0, 2 ** 16, 4000).astype(np.uint32) << 16 | 0x8000).view(np.float32),
+    ])
+    v = v[np.isfinite(v)]
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_round(v.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------------------------
+# routing
+# ---------------------------------------------------------------------------------------------
+
+def test_route_hand_cases():
+    ids, w = oracle.route_topk(np.array([[1.0, 3.0, 3.0, -1.0]], dtype=np.float32), 2)
+    assert ids.tolist() == [[1, 2]] and w.tolist() == [[0.5, 0.5]]
+    ids, w = oracle.route_topk(np.array([[1.0, 3.0, 3.0, -1.0]], dtype=np.float32), 1)
+    assert ids.tolist() == [[1]] and w.tolist() == [[1.0]]
+    for k in (1, 2, 4):
+        ids, w = oracle.route_topk(np.full((3, 8), 0.25, dtype=np.float32), k)
+        assert ids.tolist() == [list(range(k))] * 3
+        assert np.all(w == np.float32(1.0 / k))
+    # -0.0 and +0.0 are equal: the lower id wins
+    ids, _ = oracle.route_topk(np.array([[-1.0, 0.0, -0.0, -2.0]], dtype=np.float32), 2)
+    assert ids.tolist() == [[1, 2]]
+    ids, _ = oracle.route_topk(np.array([[-1.0, -0.0, 0.0, -2.0]], dtype=np.float32), 2)
+    assert ids.tolist() == [[1, 2]]
+
+
+def test_route_two_experts_closed_form():
+    # k=2 softmax: w1 = 1 / (1 + e^(l0 - l1)); with l0 - l1 = ln 3, w = (3/4, 1/4) exactly
+    l0 = np.float32(0.5)
+    l1 = np.float32(0.5 - math.log(3.0))
+    ids, w = oracle.route_topk(np.array([[l1, l0, -5.0]], dtype=np.float32), 2)
+    assert ids.tolist() == [[1, 0]]
+    d = float(l0) - float(l1)                     # ln 3 up to f32 rounding of l1
+    assert abs(float(w[0, 0]) - 1 / (1 + math.exp(-d))) < 1e-7
+    assert abs(float(w[0, 1]) - 0.25) < 1e-6
+
+
+@pytest.mark.parametrize("E,k,seed", [(4, 2, 0), (32, 4, 1), (128, 4, 2), (16, 16, 3), (7, 3, 4)])
+def test_route_against_full_sort_and_exact_softmax(E, k, seed):
+    # ids: brute force = full sort by (value desc, id asc); weights: softmax evaluated with
+    # 40-digit decimal exp, compared within half an f32 ulp (+ the float64 evaluation error)
+    g = np.random.default_rng(seed)
+    logits = (np.round(g.standard_normal((40, E)) * 4) / 4).astype(np.float32)   # many ties
+    ids, w = oracle.route_topk(logits, k)
+    getcontext().prec = 40
+    for t in range(logits.shape[0]):
+        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
+        assert ids[t].tolist() == order
+        ex = [Decimal(float(logits[t, e])).exp() for e in order]
+        tot = sum(ex)
+        for s in range(k):
+            exact = float(ex[s] / tot)
+            ulp = float(np.spacing(np.float32(exact)))
+            assert abs(float(w[t, s]) - exact) <= 0.5 * ulp * (1 + 1e-6) + 1e-300
+
+
+# ---------------------------------------------------------------------------------------------
+# bucket / CSR
+# ---------------------------------------------------------------------------------------------
+
+def test_bucket_hand_case():
+    ids = np.array([[2, 0], [0, 3], [2, 3]], dtype=np.int32)
+    mpad = oracle.mpad_max(3, 2, 4, 4)
+    assert mpad == 20                       # roundup(6 + 4*3, 4)
+    counts, basep, row_tok, pos = oracle.bucket(ids, 4, 4, mpad)
+    assert counts.tolist() == [2, 0, 2, 2]
+    assert basep.tolist() == [0, 4, 4, 8, 12]
+    assert row_tok.tolist() == [0, 1, -1, -1, 0, 2, -1, -1, 1, 2, -1, -1] + [-1] * 8
+    assert pos.tolist() == [[4, 0], [1, 8], [5, 9]]
+
+
+def check_csr_invariants(ids, E, tile_m, mpad, counts, basep, row_tok, pos):
+    T, k = ids.shape
+    assert counts.sum() == T * k
+    for e in range(E):
+        assert counts[e] == int((ids == e).sum())
+        assert basep[e] % tile_m == 0
+        assert basep[e + 1] - basep[e] == -(-counts[e] // tile_m) * tile_m
+    assert basep[0] == 0 and basep[E] <= mpad
+    seen = set()
+    for t in range(T):
+        for s in range(k):
+            r = pos[t, s]
+            e = ids[t, s]
+            assert basep[e] <= r < basep[e] + counts[e]
+            assert row_tok[r] == t
+            assert r not in seen
+            seen.add(r)
+    assert int((row_tok == -1).sum()) == mpad - T * k
+    for e in range(E):
+        toks = row_tok[basep[e]:basep[e] + counts[e]]
+        assert np.all(np.diff(toks) > 0), "rows of a bucket in ascending token order"
+        assert np.all(row_tok[basep[e] + counts[e]:basep[e + 1]] == -1)
+    assert np.all(row_tok[basep[E]:] == -1)
+
+
+@pytest.mark.parametrize("T,k,E,tile_m,skew", [(8, 2, 4, 16, 0.0), (64, 4, 32, 16, 3.0),
+                                               (100, 4, 32, 1, 0.0), (37, 3, 5, 7, 1.0),
+                                               (200, 4, 128, 32, 0.0), (5, 1, 1, 4, 0.0)])
+def test_bucket_invariants(T, k, E, tile_m, skew):
+    ids = synth.random_ids(T * 131 + E, T, k, E, skew=skew)
+    mpad = oracle.mpad_max(T, k, E, tile_m)
+    out = oracle.bucket(ids, E, tile_m, mpad)
+    check_csr_invariants(ids, E, tile_m, mpad, *out)
+
+
+def test_mpad_max_is_reached_by_the_worst_case():
+    # every expert gets exactly one row (the most padding possible): basep[E] == mpad_max
+    for E, tile_m in [(4, 16), (32, 16), (7, 5)]:
+        ids = np.arange(E, dtype=np.int32)[:, None]
+        mpad = oracle.mpad_max(E, 1, E, tile_m)
+        assert mpad == E * tile_m
+        _, basep, _, _ = oracle.bucket(ids, E, tile_m, mpad)
+        assert basep[E] == mpad
+    # fewer rows than experts: at most R experts are non-empty
+    assert oracle.mpad_max(1, 4, 32, 16) == 64
+    assert oracle.mpad_max(1, 4, 32, 1) == 4
+    assert oracle.mpad_max(512, 4, 32, 16) == 2048 + 32 * 16 - 32
+
+
+# ---------------------------------------------------------------------------------------------
+# projections
+# ---------------------------------------------------------------------------------------------
+
+def test_projection_hand_case():
+    # W row 0: elements (0.5, 1.0, -1.0, 0, ...) * 2^(128-127); x = (2, -1, 0.5, 0, ...)
+    # g[0] = 0.25 + 2*1 + (-1)*2 + 0.5*(-2) = -0.75; row 1 is all zero codes: g[1] = bias = -1
+    q = np.zeros((1, 2, 16), dtype=np.uint8)
+    q[0, 0, 0] = 0x21
+    q[0, 0, 1] = 0x0A
+    s = np.full((1, 2, 1), 128, dtype=np.uint8)
+    bias = np.array([[0.25, -1.0]], dtype=np.float32)
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, :3] = [2.0, -1.0, 0.5]
+    xb = synth.round_f32_to_bf16_bits(x)
+    counts, basep = np.array([1]), np.array([0, 1])
+    out, S = oracle.project(xb, None, q, s, bias, counts, basep, 1)
+    assert out.tolist() == [[-0.75, -1.0]]
+    assert S.tolist() == [[0.25 + 2 + 2 + 1, 1.0]]
+    # the same through a gather map and a padded CSR
+    out2, _ = oracle.project(np.concatenate([np.zeros((2, 32), np.uint16), xb]),
+                             np.array([2, -1, -1, -1]), q, s, bias, counts,
+                             np.array([0, 4]), 4)
+    assert out2[0].tolist() == [-0.75, -1.0] and np.all(np.isnan(out2[1:]))
+
+
+def brute_force_projection(xb, a_row, q, s, bias, counts, basep):
+    """Exact rational projection by per-element loops over the packed bytes."""
+    E, N, _ = q.shape
+    K = q.shape[2] * 2
+    res = {}
+    for e in range(E):
+        for j in range(int(counts[e])):
+            r = int(basep[e]) + j
+            x = xb[r if a_row is None else int(a_row[r])]
+            for n in range(N):
+                acc = Fraction(float(bias[e, n])) if bias is not None else Fraction(0)
+                for i in range(K):
+                    sign, mag = e2m1_bits(element_code(q[e, n], i))
+                    acc += bf16_fraction(x[i]) * sign * mag * Fraction(2) ** (int(s[e, n, i // 32]) - 127)
+                res[(r, n)] = acc
+    return res
+
+
+def exact_case(seed, T=5, k=2, E=3, N=6, K=64, tile_m=4):
+    g = np.random.default_rng(seed)
+    xb = synth.round_f32_to_bf16_bits(g.integers(-4, 5, (T, K)).astype(np.float32))
+    q = g.integers(0, 256, (E, N, K // 2)).astype(np.uint8)
+    s = g.integers(126, 128, (E, N, K // 32)).astype(np.uint8)
+    bias = (g.integers(-8, 9, (E, N)) / 4).astype(np.float32)
+    ids = synth.random_ids(seed, T, k, E)
+    mpad = oracle.mpad_max(T, k, E, tile_m)
+    counts, basep, row_tok, pos = oracle.bucket(ids, E, tile_m, mpad)
+    return xb, q, s, bias, counts, basep, row_tok, mpad
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_projection_exact_arithmetic_brute_force(seed):
+    # integer activations, scales 2^-1/2^0, biases in quarters: every partial sum is exact, so
+    # the float64 oracle must equal rational brute force exactly. Catches a transposed weight,
+    # a wrong gather, a scale on the wrong block, a dropped bias, or a wrong expert offset.
+    xb, q, s, bias, counts, basep, row_tok, mpad = exact_case(seed)
+    out, _ = oracle.project(xb, row_tok, q, s, bias, counts, basep, mpad)
+    ref = brute_force_projection(xb, row_tok, q, s, bias, counts, basep)
+    for (r, n), v in ref.items():
+        assert Fraction(float(out[r, n])) == v, (r, n)
+    live = {r for r, _ in ref}
+    for r in range(mpad):
+        if r not in live:
+            assert np.all(np.isnan(out[r]))
+    # the sampled variant gives the same numbers
+    samples = list(ref.keys())[::3]
+    vals, _ = oracle.project_at(xb, row_tok, q, s, bias, counts, basep, samples)
+    for (r, n), v in zip(samples, vals):
+        assert Fraction(float(v)) == ref[(r, n)]
+
+
+def test_projection_error_bound_of_fp32_accumulation():
+    # a plain fp32 accumulation in sequential order must sit within gamma_K * S of the oracle
+    # (the closed-form bound behind the 1e-3*S + 1e-5 tolerance); S itself must bound |out|
+    wl = synth.WORKLOADS["tiny"]
+    W = synth.layer_weights(wl)["gate_up"]
+    tok = synth.tokens(wl)
+    K = wl.dim
+    ids, _ = oracle.route_topk(tok["logits"], wl.k)
+    mpad = oracle.mpad_max(wl.T, wl.k, wl.E, wl.tile_m)
+    counts, basep, row_tok, _ = oracle.bucket(ids, wl.E, wl.tile_m, mpad)
+    out, S = oracle.project(tok["x"], row_tok, W["q"], W["s"], W["bias"], counts, basep, mpad)
+    u = 2.0 ** -24
+    gamma = (K + 1) * u / (1 - (K + 1) * u)
+    x32 = synth.bf16_bits_to_f32(tok["x"])
+    for e, r in oracle.live_rows(counts, basep):
+        Wd = oracle.dequant(W["q"][e], W["s"][e])
+        for n in range(0, W["q"].shape[1], 7):
+            acc = np.float32(W["bias"][e, n])
+            for i in range(K):
+                acc = np.float32(acc + np.float32(x32[row_tok[r], i] * Wd[n, i]))
+            assert abs(float(acc) - out[r, n]) <= gamma * S[r, n]
+            assert abs(out[r, n]) <= S[r, n]
+
+
+# ---------------------------------------------------------------------------------------------
+# SwiGLU-OAI
+# ---------------------------------------------------------------------------------------------
+
+def test_swiglu_closed_forms():
+    ln3 = math.log(3.0) / ALPHA            # sigmoid(alpha * ln3) = 3/4, sigmoid(-alpha*ln3) = 1/4
+    g = np.array([[0.0, 0.0, 3.0, -2.0],   # gate 0 -> 0 whatever up is (row = gate | up)
+                  [2.0, 1.5, -1.0, -1.0],  # up -1 -> 0 whatever gate is
+                  [ln3, -ln3, 1.0, 1.0],   # known sigmoids, up + 1 = 2
+                  [100.0, 7.0, 0.5, 0.5],  # gate clamps at +limit
+                  [ln3, ln3, 100.0, -100.0]], dtype=np.float64)   # up clamps at +-limit
+    h = oracle.swiglu_oai(g, ALPHA, LIMIT)
+    assert h.shape == (5, 2)
+    assert h[0].tolist() == [0.0, 0.0]
+    assert h[1].tolist() == [0.0, 0.0]
+    assert h[2, 0] == pytest.approx(ln3 * 0.75 * 2.0, rel=1e-15)
+    assert h[2, 1] == pytest.approx(-ln3 * 0.25 * 2.0, rel=1e-15)
+    assert h[3, 0] == h[3, 1]
+    assert h[3, 0] == pytest.approx(7.0 / (1 + math.exp(-ALPHA * 7.0)) * 1.5, rel=1e-15)
+    assert h[4, 0] == pytest.approx(ln3 * 0.75 * 8.0, rel=1e-15)
+    assert h[4, 1] == pytest.approx(ln3 * 0.75 * -6.0, rel=1e-15)
+    # gate is not clamped from below: a very negative gate drives h to (-)0
+    assert abs(oracle.swiglu_oai(np.array([[-60.0, 3.0]]), ALPHA, LIMIT)[0, 0]) < 1e-40
+
+
+# ---------------------------------------------------------------------------------------------
+# combine
+# ---------------------------------------------------------------------------------------------
+
+def test_combine_hand_cases():
+    d = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0]])
+    y, S = oracle.combine(d, np.array([[2, 0]]), np.array([[0.25, 0.75]], dtype=np.float32))
+    assert y.tolist() == [[2.0, 3.0]] and S.tolist() == [[2.0, 3.0]]
+    y, _ = oracle.combine(d, np.array([[1], [0], [2]]), np.ones((3, 1), dtype=np.float32))
+    assert y.tolist() == [[3.0, 4.0], [1.0, 2.0], [5.0, 6.0]]
+    y, S = oracle.combine(-d, np.array([[0, 1]]), np.array([[0.5, 0.5]], dtype=np.float32))
+    assert y.tolist() == [[-2.0, -3.0]] and S.tolist() == [[2.0, 3.0]]
+
+
+# ---------------------------------------------------------------------------------------------
+# whole chain on the tiny workload: against its stored oracle outputs (a regression record
+# written by tests/golden/make_golden.py, which runs only the oracle)
+# ---------------------------------------------------------------------------------------------
+
+def test_chain_tiny_matches_golden_record():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_chain.npz")
+    gold = np.load(path)
+    wl = synth.WORKLOADS["tiny"]
+    tok = synth.tokens(wl)
+    W = synth.layer_weights(wl)
+    out = oracle.chain(tok["x"], tok["logits"], W["gate_up"], W["down"], wl.k, wl.tile_m,
+                       synth.ALPHA, synth.LIMIT)
+    for key in ("ids", "w", "counts", "basep", "row_tok", "pos", "h"):
+        assert np.array_equal(out[key], gold[key]), key
+    for key in ("g", "d", "y"):
+        assert np.array_equal(out[key], gold[key], equal_nan=True), key
+
+
+def test_synthetic_inputs_have_the_workload_distributions():
+    wl = synth.WORKLOADS["tiny"]
+    W = synth.layer_weights(wl)
+    codes = oracle.unpack_codes(W["gate_up"]["q"])
+    assert set(np.unique(codes).tolist()) == set(range(16))
+    assert W["gate_up"]["s"].min() >= 118 and W["gate_up"]["s"].max() <= 124
+    assert W["gate_up"]["q"].shape == (4, 128, 32) and W["down"]["q"].shape == (4, 64, 32)
+    tok = synth.tokens(synth.WORKLOADS["prefill_120b_t2048"])
+    assert len(tok["dead"]) == 8 and np.all(tok["logits"][:, tok["dead"]] == -30.0)
+    # the same seed regenerates the same arrays
+    assert np.array_equal(synth.layer_weights(wl)["down"]["q"], W["down"]["q"])
