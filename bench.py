@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MXFP4 MoE chain on one MI355X (gfx950).
+
+A step is one pass of the whole chain (route -> bucket -> gate_up + SwiGLU-OAI -> down ->
+combine) over one batch. The headline workload is gpt-oss-20b-shaped decode: E=32 experts,
+dim = ffn = 2880, top-4, one token, through 24 distinct seeded MoE layers (10.15 GB of MXFP4
+experts resident in HBM, 1.27 GB touched per step, far more than the 256 MB last-level cache), so a
+step is one decode token through the model's 24 MoE layers, replayed as one HIP graph.
+
+Prints ONE JSON line. `value` = decode tokens/s through the 24-layer stack. The same line also
+carries the dominant kernel's roofline (its average duration from HIP events recorded around
+each launch on the stream it runs on), the decode weight GB/s of the two MXFP4 GEMVs, the pp512
+prefill expert-GEMM TFLOP/s (gpt-oss-20b shape, T=512, bf16 MFMA), and the CPU oracle timed on a
+bounded sample of the decode workload on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_DENSE_TFLOPS = 2500.0      # MI355X bf16 dense MFMA
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--kernel-reps", type=int, default=4, help="passes of per-launch event timing")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=12.0)
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Layer:
+    """One MoE layer resident on the GPU with preallocated intermediates (graph-capturable)."""
+
+    def __init__(self, moe, synth, torch, wl, l, kernel, W=None, tok=None):
+        self.moe, self.wl = moe, wl
+        tok = tok if tok is not None else synth.tokens(wl, l)
+        W = W if W is not None else synth.layer_weights(wl, l)
+        dev = "cuda"
+        self.x = torch.from_numpy(tok["x"].view("int16")).to(dev).view(torch.bfloat16)
+        self.logits = torch.from_numpy(tok["logits"]).to(dev)
+        self.GU = moe.MX4Experts.from_numpy(W["gate_up"], dev)
+        self.DN = moe.MX4Experts.from_numpy(W["down"], dev)
+        T, E, k, D, F = wl.T, wl.E, wl.k, wl.dim, wl.ffn
+        self.mpad = moe.moe_mpad_max(T, k, E, wl.tile_m)
+        i32, f32 = torch.int32, torch.float32
+        self.ids = torch.empty((T, k), dtype=i32, device=dev)
+        self.w = torch.empty((T, k), dtype=f32, device=dev)
+        self.csr = (torch.empty(E, dtype=i32, device=dev), torch.empty(E + 1, dtype=i32, device=dev),
+                    torch.empty(self.mpad, dtype=i32, device=dev),
+                    torch.empty((T, k), dtype=i32, device=dev))
+        self.h = torch.empty((self.mpad, F), dtype=torch.bfloat16, device=dev)
+        self.d = torch.empty((self.mpad, D), dtype=f32, device=dev)
+        self.y = torch.empty((T, D), dtype=f32, device=dev)
+        self.proj = moe.mx4_moe_gemm if kernel == "gemm" else moe.mx4_moe_gemv
+
+    def route_bucket(self):
+        m, wl = self.moe, self.wl
+        m.moe_route_topk(self.logits, wl.k, ids=self.ids, w=self.w)
+        m.moe_bucket(self.ids, wl.E, wl.tile_m, self.mpad, out=self.csr)
+
+    def gate_up(self):
+        c = self.csr
+        self.proj(self.x, c[2], self.GU, c[0], c[1], self.wl.tile_m, self.mpad,
+                  self.moe.MOE_ACT_SWIGLU_OAI, 1.702, 7.0, out=self.h)
+
+    def down(self):
+        c = self.csr
+        self.proj(self.h, None, self.DN, c[0], c[1], self.wl.tile_m, self.mpad,
+                  self.moe.MOE_ACT_NONE, 1.702, 7.0, out=self.d)
+
+    def combine(self):
+        self.moe.moe_combine(self.d, self.csr[3], self.w, out=self.y)
+
+    def chain(self):
+        self.route_bucket()
+        self.gate_up()
+        self.down()
+        self.combine()
+
+
+def build_layers(moe, synth, torch, wl, kernel, n_layers):
+    out = []
+
+    def gen(l):
+        return l, synth.layer_weights(wl, l), synth.tokens(wl, l)
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        for l, W, tok in ex.map(gen, range(n_layers)):
+            out.append(Layer(moe, synth, torch, wl, l, kernel, W=W, tok=tok))
+            del W, tok
+    torch.cuda.synchronize()
+    return out
+
+
+def sleep_cycles_for(torch, ms):
+    """Cycle count for torch.cuda._sleep lasting about `ms` (calibrated once), or 0 if absent."""
+    if not hasattr(torch.cuda, "_sleep"):
+        return 0
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    s.record()
+    torch.cuda._sleep(1_000_000)
+    e.record()
+    torch.cuda.synchronize()
+    per_ms = 1_000_000 / max(s.elapsed_time(e), 1e-3)
+    return int(per_ms * ms)
+
+
+def graph_time(torch, fn, steps, warmup):
+    """Capture fn() as one HIP graph, replay warmup + timed steps; seconds for the timed ones."""
+    fn()                                  # eager first call (one-time library set-up)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, g
+
+
+def kernel_times_us(torch, layers, stages, reps, sleep_cycles):
+    """Average duration (us) of each stage's kernel from HIP events recorded around every launch
+    on the launching stream. A sleep kernel first keeps the GPU busy so the host can queue the
+    launches ahead of it (no host-submission gaps inside the event pairs)."""
+    ev = {name: [] for name in stages}
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        if sleep_cycles:
+            torch.cuda._sleep(sleep_cycles)
+        for L in layers:
+            L.route_bucket()
+            for name in stages:
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                getattr(L, name)()
+                e.record()
+                ev[name].append((s, e))
+            L.combine()
+    torch.cuda.synchronize()
+    return {name: 1000.0 * sum(s.elapsed_time(e) for s, e in v) / len(v) for name, v in ev.items()}
+
+
+def touched_experts(torch, layers):
+    return [int(torch.unique(L.ids).numel()) for L in layers]
+
+
+def cpu_baseline(synth, wl, budget_s):
+    """The CPU oracle (as it stands) on one decode token per layer, as many layers as fit in the
+    budget, on one host thread; scaled to the 24-layer stack's tokens/s."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    times = []
+    with threadpool_limits(limits=1):
+        t_all = time.perf_counter()
+        for l in range(wl.layers):
+            tok = synth.tokens(wl, l)
+            W = synth.layer_weights(wl, l)
+            t0 = time.perf_counter()
+            oracle.chain(tok["x"], tok["logits"], W["gate_up"], W["down"], wl.k, wl.tile_m,
+                         synth.ALPHA, synth.LIMIT)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_all > budget_s:
+                break
+    per_layer = sum(times) / len(times)
+    return {"value": round(wl.T / (per_layer * wl.layers), 4), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle.chain (float64 numpy, 1 thread) on 1 token through layers 0..{len(times) - 1} "
+                      f"of the 24-layer decode workload; {per_layer * 1e3:.0f} ms per layer, "
+                      f"scaled to 24 layers"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the expert-parallel "
+              "multi-GPU path is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np  # noqa: F401
+    import torch
+    from mxfp4_mixture_experts_route_amd import _lib as moe
+    from mxfp4_mixture_experts_route_amd import synth
+    moe.lib()   # fail loudly if the HIP library is missing
+    torch.cuda.init()
+    sleep_cycles = sleep_cycles_for(torch, 20.0)
+
+    # ---------------- headline: decode, T=1, 24 MoE layers ----------------
+    wl = synth.WORKLOADS["decode_t1"]
+    log(f"building {wl.layers} layers of {wl.desc}")
+    layers = build_layers(moe, synth, torch, wl, "gemv", wl.layers)
+    step = lambda: [L.chain() for L in layers]   # noqa: E731
+    log(f"timing {args.steps} graph-replayed steps after {args.warmup} warmup")
+    secs, _ = graph_time(torch, step, args.steps, args.warmup)
+    ms_per_step = 1000.0 * secs / args.steps
+    tokens_per_s = wl.T * args.steps / secs
+
+    log("per-launch kernel timing (HIP events)")
+    kt = kernel_times_us(torch, layers, ("gate_up", "down"), args.kernel_reps, sleep_cycles)
+    n_touch = touched_experts(torch, layers)
+    per_expert_gu = 2 * wl.ffn * wl.dim * 17 // 32          # nibbles + scales, bytes
+    per_expert_dn = wl.dim * wl.ffn * 17 // 32
+    avg_touch = sum(n_touch) / len(n_touch)
+    gu_bytes = avg_touch * per_expert_gu
+    dn_bytes = avg_touch * per_expert_dn
+    gu_gbps = gu_bytes / (kt["gate_up"] * 1e3)
+    wgbps = (gu_bytes + dn_bytes) / ((kt["gate_up"] + kt["down"]) * 1e3)
+
+    result = {
+        "metric": "MoE chain tokens/s; decode mx4 weight GB/s; pp512 expert GEMM TFLOP/s (1 GPU)",
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gpt-oss-20b-shaped decode, T=1, 24 distinct MoE layers per step",
+                   "E": wl.E, "dim": wl.dim, "ffn": wl.ffn, "k": wl.k, "T": wl.T,
+                   "layers": wl.layers, "tile_m": wl.tile_m, "weights": "mxfp4",
+                   "accumulate": "f32", "projection": "mx4_moe_gemv", "graph": "hip graph replay"},
+        "roofline": {"kernel": "mx4_moe_gemv gate_up + SwiGLU-OAI", "bound": "hbm",
+                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(kt["gate_up"], 3)},
+        "decode": {"weight_GBps_gemv_pair": round(wgbps, 1),
+                   "frac_hbm_peak": round(wgbps / HBM_PEAK_GBPS, 4),
+                   "gate_up_us": round(kt["gate_up"], 3), "down_us": round(kt["down"], 3),
+                   "touched_experts_per_layer": avg_touch,
+                   "per_layer_chain_us": round(ms_per_step * 1000.0 / wl.layers, 3)},
+    }
+    del layers
+    torch.cuda.empty_cache()
+
+    # ---------------- pp512 prefill expert GEMM ----------------
+    if not args.no_prefill:
+        pw = synth.WORKLOADS["prefill_pp512"]
+        log(f"building {pw.layers} layers of {pw.desc}")
+        players = build_layers(moe, synth, torch, pw, "gemm", pw.layers)
+        psecs, _ = graph_time(torch, lambda: [L.chain() for L in players], max(5, args.steps // 5),
+                              args.warmup)
+        p_steps = max(5, args.steps // 5)
+        pkt = kernel_times_us(torch, players, ("gate_up", "down"), args.kernel_reps, sleep_cycles)
+        R = pw.T * pw.k
+        flops = 2.0 * R * pw.dim * 3 * pw.ffn
+        tflops = flops / ((pkt["gate_up"] + pkt["down"]) * 1e-6) / 1e12
+        result["prefill_pp512"] = {
+            "expert_gemm_TFLOPs": round(tflops, 1),
+            "frac_bf16_peak": round(tflops / BF16_DENSE_TFLOPS, 4),
+            "gate_up_us": round(pkt["gate_up"], 2), "down_us": round(pkt["down"], 2),
+            "chain_tokens_per_s": round(pw.T * pw.layers * p_steps / psecs, 1),
+            "per_layer_chain_us": round(1e6 * psecs / (p_steps * pw.layers), 2),
+            "flops_per_layer": flops,
+        }
+        del players
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(synth, wl, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,232 @@
+"""ctypes binding of libmoe_mx4.so: the C ABI declared in include/moe_mx4.h, same names.
+
+Argument marshalling only: each function checks tensor dtypes/devices, allocates missing
+outputs with torch (device memory is PyTorch's job), and calls the C entry point on the current
+HIP stream. Every step of the chain runs in the library's kernels; there is no fallback — if the
+library is missing, loading fails with an error that says how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_mx4.so")
+
+MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_ELAUNCH = 0, 1, 2, 3, 4
+MOE_ACT_NONE, MOE_ACT_SWIGLU_OAI = 0, 1
+MOE_MAX_K, MOE_MAX_E, MOE_MAX_TILE_M = 16, 1024, 256
+
+EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_moe_gemv",
+           "mx4_moe_gemm", "moe_combine")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({strerror(status)})")
+
+
+class Mx4ExpertsC(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("E", ctypes.c_int), ("N", ctypes.c_int), ("K", ctypes.c_int)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mxfp4_mixture_experts_route_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci, cf = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        L.moe_strerror.restype = ctypes.c_char_p
+        L.moe_strerror.argtypes = [ci]
+        L.moe_mpad_max.restype = i64
+        L.moe_mpad_max.argtypes = [i64, ci, ci, ci]
+        L.moe_route_topk.restype = ci
+        L.moe_route_topk.argtypes = [vp, i64, ci, ci, vp, vp, vp]
+        L.moe_bucket.restype = ci
+        L.moe_bucket.argtypes = [vp, i64, ci, ci, ci, i64, vp, vp, vp, vp, vp]
+        proj = [vp, vp, i64, ctypes.POINTER(Mx4ExpertsC), vp, vp, ci, i64, ci, cf, cf, vp, vp]
+        for name in ("mx4_moe_gemv", "mx4_moe_gemm"):
+            getattr(L, name).restype = ci
+            getattr(L, name).argtypes = proj
+        L.moe_combine.restype = ci
+        L.moe_combine.argtypes = [vp, i64, vp, vp, i64, ci, ci, vp, vp]
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().moe_strerror(int(status)).decode()
+
+
+def moe_mpad_max(T: int, k: int, E: int, tile_m: int) -> int:
+    return int(lib().moe_mpad_max(int(T), int(k), int(E), int(tile_m)))
+
+
+# ---------------------------------------------------------------------------------------------
+# torch-facing wrappers
+# ---------------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, dtype, name):
+    torch = _torch()
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise TypeError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    del torch
+
+
+def _call(fn: str, *args):
+    st = getattr(lib(), fn)(*args)
+    if st != MOE_OK:
+        raise MoeError(fn, st)
+
+
+class MX4Experts:
+    """A device-resident MXFP4 expert stack: q u8 [E][N][K/2], s u8 [E][N][K/32], bias f32 [E][N]
+    (or None). Holds the tensors alive and builds the C descriptor."""
+
+    def __init__(self, q, s, bias=None):
+        torch = _torch()
+        _check(q, torch.uint8, "q")
+        _check(s, torch.uint8, "s")
+        E, N, half_k = q.shape
+        K = half_k * 2
+        if tuple(s.shape) != (E, N, K // 32):
+            raise ValueError(f"s: expected shape {(E, N, K // 32)}, got {tuple(s.shape)}")
+        if bias is not None:
+            _check(bias, torch.float32, "bias")
+            if tuple(bias.shape) != (E, N):
+                raise ValueError(f"bias: expected shape {(E, N)}")
+        self.q, self.s, self.bias = q, s, bias
+        self.E, self.N, self.K = E, N, K
+        self.c = Mx4ExpertsC(q.data_ptr(), s.data_ptr(),
+                             None if bias is None else bias.data_ptr(), E, N, K)
+
+    @classmethod
+    def from_numpy(cls, d: dict, device="cuda"):
+        torch = _torch()
+        q = torch.from_numpy(d["q"]).to(device)
+        s = torch.from_numpy(d["s"]).to(device)
+        b = None if d.get("bias") is None else torch.from_numpy(d["bias"]).to(device)
+        return cls(q, s, b)
+
+    @property
+    def nbytes(self) -> int:
+        return self.q.numel() + self.s.numel()
+
+
+def moe_route_topk(logits, k: int, ids=None, w=None, stream=None):
+    """ids i32 [T][k], w f32 [T][k] = top-k routing of f32 logits [T][E]."""
+    torch = _torch()
+    _check(logits, torch.float32, "logits")
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device) if ids is None else ids
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device) if w is None else w
+    _call("moe_route_topk", _ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(stream))
+    return ids, w
+
+
+def moe_bucket(ids, E: int, tile_m: int, mpad_max: int | None = None, out=None, stream=None):
+    """(counts [E], basep [E+1], row_tok [mpad_max], pos [T][k]) of i32 ids [T][k]."""
+    torch = _torch()
+    _check(ids, torch.int32, "ids")
+    T, k = ids.shape
+    if mpad_max is None:
+        mpad_max = moe_mpad_max(T, k, E, tile_m)
+    if out is None:
+        dev = ids.device
+        out = (torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(mpad_max, dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.int32, device=dev))
+    counts, basep, row_tok, pos = out
+    _call("moe_bucket", _ptr(ids), T, k, E, tile_m, mpad_max, _ptr(counts), _ptr(basep),
+          _ptr(row_tok), _ptr(pos), _stream(stream))
+    return counts, basep, row_tok, pos
+
+
+def _projection(fn, a, a_row, w: MX4Experts, counts, basep, tile_m, mpad_max, act, alpha, limit,
+                out, stream):
+    torch = _torch()
+    _check(a, torch.int16 if a.dtype == torch.int16 else torch.bfloat16, "a")
+    if a_row is not None:
+        _check(a_row, torch.int32, "a_row")
+    _check(counts, torch.int32, "counts")
+    _check(basep, torch.int32, "basep")
+    if out is None:
+        if act == MOE_ACT_SWIGLU_OAI:
+            out = torch.empty((mpad_max, w.N // 2), dtype=torch.bfloat16, device=a.device)
+        else:
+            out = torch.empty((mpad_max, w.N), dtype=torch.float32, device=a.device)
+    _call(fn, _ptr(a), _ptr(a_row), a.shape[0], ctypes.byref(w.c), _ptr(counts), _ptr(basep),
+          tile_m, mpad_max, act, float(alpha), float(limit), _ptr(out), _stream(stream))
+    return out
+
+
+def mx4_moe_gemv(a, a_row, w, counts, basep, tile_m, mpad_max, act=MOE_ACT_NONE, alpha=1.702,
+                 limit=7.0, out=None, stream=None):
+    return _projection("mx4_moe_gemv", a, a_row, w, counts, basep, tile_m, mpad_max, act, alpha,
+                       limit, out, stream)
+
+
+def mx4_moe_gemm(a, a_row, w, counts, basep, tile_m, mpad_max, act=MOE_ACT_NONE, alpha=1.702,
+                 limit=7.0, out=None, stream=None):
+    return _projection("mx4_moe_gemm", a, a_row, w, counts, basep, tile_m, mpad_max, act, alpha,
+                       limit, out, stream)
+
+
+def moe_combine(d, pos, w, out=None, stream=None):
+    """y f32 [T][D] = slot-order routing-weighted sum of d rows."""
+    torch = _torch()
+    _check(d, torch.float32, "d")
+    _check(pos, torch.int32, "pos")
+    _check(w, torch.float32, "w")
+    T, k = pos.shape
+    D = d.shape[1]
+    y = torch.empty((T, D), dtype=torch.float32, device=d.device) if out is None else out
+    _call("moe_combine", _ptr(d), d.shape[0], _ptr(pos), _ptr(w), T, k, D, _ptr(y),
+          _stream(stream))
+    return y
+
+
+def moe_layer(x, logits, gate_up: MX4Experts, down: MX4Experts, k: int, tile_m: int,
+              alpha: float = 1.702, limit: float = 7.0, projection: str = "gemm", stream=None):
+    """One routed-expert MoE layer: route -> bucket -> gate_up+SwiGLU -> down -> combine.
+    Returns a dict of every intermediate (device tensors)."""
+    T, E = logits.shape
+    fn = mx4_moe_gemm if projection == "gemm" else mx4_moe_gemv
+    ids, w = moe_route_topk(logits, k, stream=stream)
+    mpad = moe_mpad_max(T, k, E, tile_m)
+    counts, basep, row_tok, pos = moe_bucket(ids, E, tile_m, mpad, stream=stream)
+    h = fn(x, row_tok, gate_up, counts, basep, tile_m, mpad, MOE_ACT_SWIGLU_OAI, alpha, limit,
+           stream=stream)
+    d = fn(h, None, down, counts, basep, tile_m, mpad, MOE_ACT_NONE, alpha, limit, stream=stream)
+    y = moe_combine(d, pos, w, stream=stream)
+    return {"ids": ids, "w": w, "mpad": mpad, "counts": counts, "basep": basep,
+            "row_tok": row_tok, "pos": pos, "h": h, "d": d, "y": y}

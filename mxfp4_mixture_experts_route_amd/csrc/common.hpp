@@ -1,0 +1,95 @@
+// Device-side helpers shared by the kernels of the routed MXFP4 MoE chain (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_mx4.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// e8m0 exponent byte -> the fp32 value 2^(e-127): e << 23 is the normal encoding for e >= 1,
+// e == 0 is the subnormal 2^-127 (0x00400000), and e == 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  uint32_t bits = e ? (e << 23) : 0x00400000u;
+  bits = (e == 255u) ? 0x7FC00000u : bits;
+  return __uint_as_float(bits);
+}
+
+// float -> bf16 bit pattern, round to nearest even (NaN -> quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Reinterpret a dword as two bf16 (element 0 = low half). Take the dword as a scalar first:
+// clang (ROCm 7.2) miscompiles __builtin_bit_cast applied directly to an ext-vector element,
+// reading element 0 whatever the index.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) {
+  bf16x2_t r;
+  __builtin_memcpy(&r, &u, sizeof(r));
+  return r;
+}
+
+// Clamped SwiGLU-OAI of one (gate, up) pair: gc = min(gate, limit), uc = clamp(up, +-limit),
+// gc * sigmoid(alpha*gc) * (uc + 1). The sigmoid is evaluated on the side where exp() cannot
+// overflow, so very negative gates give correctly tiny (not zero-by-overflow) results.
+__device__ __forceinline__ float swiglu_oai(float gate, float up, float alpha, float limit) {
+  float gc = fminf(gate, limit);
+  float uc = fminf(fmaxf(up, -limit), limit);
+  float z = alpha * gc;
+  float ez = expf(-fabsf(z));
+  float sig = (z >= 0.0f) ? 1.0f / (1.0f + ez) : ez / (1.0f + ez);
+  return gc * sig * (uc + 1.0f);
+}
+
+// Sum over the 16 lanes of each DPP row (lanes 16r..16r+15); every lane gets the row's sum.
+// Fixed butterfly order, so the result is deterministic.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __shfl_xor(v, 8, 16);
+  v += __shfl_xor(v, 4, 16);
+  v += __shfl_xor(v, 2, 16);
+  v += __shfl_xor(v, 1, 16);
+  return v;
+}
+
+// Index of the slot-th expert with a non-zero count, or -1; computed by every thread of the
+// block (the block's threads scan counts[] together). Needs blockDim.x == 256 and a
+// __shared__ int scratch[2].
+__device__ __forceinline__ int slot_expert(const int32_t* __restrict__ counts, int E, int slot,
+                                           int* scratch) {
+  if (threadIdx.x == 0) scratch[0] = -1;
+  __syncthreads();
+  int seen = 0;
+  for (int base = 0; base < E; base += 256) {
+    const int e = base + (int)threadIdx.x;
+    const bool live = (e < E) && (counts[e] > 0);
+    // block-wide exclusive rank of this live expert
+    const uint64_t ballot = __ballot(live);
+    const int lane = (int)(threadIdx.x & 63);
+    const int wave = (int)(threadIdx.x >> 6);
+    const int in_wave = __popcll(ballot & ((lane ? (~0ull >> (64 - lane)) : 0ull)));
+    __shared__ int wave_tot[4];
+    if (lane == 0) wave_tot[wave] = __popcll(ballot);
+    __syncthreads();
+    int before = seen;
+    for (int w = 0; w < wave; ++w) before += wave_tot[w];
+    if (live && before + in_wave == slot) scratch[0] = e;
+    seen += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+    __syncthreads();
+  }
+  return scratch[0];
+}
+
+}  // namespace moe

@@ -1,0 +1,115 @@
+"""The C ABI library on the host (no GPU): it loads, exports every function include/moe_mx4.h
+declares, computes moe_mpad_max like the oracle, and rejects bad arguments with the documented
+status before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import oracle
+from mxfp4_mixture_experts_route_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mx4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def test_library_loads_and_exports_every_declared_function():
+    L = _lib.lib()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_strerror_covers_every_status():
+    for st in range(5):
+        assert _lib.strerror(st) and _lib.strerror(st) != "unknown status"
+    assert _lib.strerror(99) == "unknown status"
+
+
+@pytest.mark.parametrize("T,k,E,tile_m", [(1, 4, 32, 1), (1, 4, 32, 16), (64, 4, 32, 16),
+                                          (512, 4, 32, 16), (2048, 4, 128, 16), (8, 2, 4, 16),
+                                          (3, 2, 4, 4), (7, 3, 5, 7), (1, 1, 1, 256)])
+def test_mpad_max_matches_oracle(T, k, E, tile_m):
+    assert _lib.moe_mpad_max(T, k, E, tile_m) == oracle.mpad_max(T, k, E, tile_m)
+
+
+def test_mpad_max_rejects_bad_arguments():
+    for args in [(0, 4, 32, 1), (1, 0, 32, 1), (1, 4, 0, 1), (1, 5, 4, 1), (1, 4, 32, 0)]:
+        assert _lib.moe_mpad_max(*args) == -1
+
+
+# The argument checks below pass fake (never dereferenced) device addresses; they only run where
+# no GPU is visible, so an unexpected pass of validation can never launch on real hardware.
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="host-only validation tests use fake device addresses")
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def experts(q=0x1000, s=0x2000, E=4, N=64, K=64):
+    return _lib.Mx4ExpertsC(q, s, None, E, N, K)
+
+
+@no_gpu
+def test_route_and_bucket_argument_checks():
+    L = _lib.lib()
+    assert L.moe_route_topk(None, 1, 4, 2, FAKE, FAKE, None) == _lib.MOE_EINVAL
+    assert L.moe_route_topk(FAKE, 0, 4, 2, FAKE, FAKE, None) == _lib.MOE_EINVAL
+    assert L.moe_route_topk(FAKE, 1, 4, 5, FAKE, FAKE, None) == _lib.MOE_EINVAL
+    assert L.moe_route_topk(FAKE, 1, 64, 17, FAKE, FAKE, None) == _lib.MOE_EINVAL
+    assert L.moe_route_topk(FAKE, 1, 2048, 4, FAKE, FAKE, None) == _lib.MOE_ESHAPE
+    ok = [FAKE] * 4
+    assert L.moe_bucket(None, 3, 2, 4, 4, 20, *ok, None) == _lib.MOE_EINVAL
+    assert L.moe_bucket(FAKE, 3, 2, 4, 4, 19, *ok, None) == _lib.MOE_ESHAPE   # mpad too small
+    assert L.moe_bucket(FAKE, 3, 2, 4, 0, 20, *ok, None) == _lib.MOE_ESHAPE
+    assert L.moe_bucket(FAKE, 3, 2, 4, 257, 5000, *ok, None) == _lib.MOE_ESHAPE
+    assert L.moe_bucket(FAKE, 3, 5, 4, 4, 20, *ok, None) == _lib.MOE_EINVAL
+
+
+@no_gpu
+@pytest.mark.parametrize("fn", ["mx4_moe_gemv", "mx4_moe_gemm"])
+def test_projection_argument_checks(fn):
+    f = getattr(_lib.lib(), fn)
+    good = experts()
+    NONE, SW = _lib.MOE_ACT_NONE, _lib.MOE_ACT_SWIGLU_OAI
+
+    def call(a=FAKE, a_row=FAKE, a_rows=8, w=good, counts=FAKE, basep=FAKE, tile_m=16,
+             mpad=64, act=NONE, out=FAKE):
+        return f(a, a_row, a_rows, None if w is None else ctypes.byref(w), counts, basep,
+                 tile_m, mpad, act, 1.702, 7.0, out, None)
+
+    assert call(a=None) == _lib.MOE_EINVAL
+    assert call(w=None) == _lib.MOE_EINVAL
+    assert call(w=experts(q=0)) == _lib.MOE_EINVAL
+    assert call(counts=None) == _lib.MOE_EINVAL
+    assert call(out=None) == _lib.MOE_EINVAL
+    assert call(act=7) == _lib.MOE_EINVAL
+    assert call(a_rows=0) == _lib.MOE_EINVAL
+    assert call(w=experts(K=48)) == _lib.MOE_ESHAPE
+    assert call(w=experts(K=16)) == _lib.MOE_ESHAPE
+    assert call(w=experts(N=63), act=SW) == _lib.MOE_ESHAPE
+    assert call(tile_m=0) == _lib.MOE_ESHAPE
+    assert call(tile_m=300) == _lib.MOE_ESHAPE
+    assert call(w=experts(E=2000)) == _lib.MOE_ESHAPE
+    assert call(a_row=None, a_rows=8, mpad=64) == _lib.MOE_ESHAPE
+    assert call(w=experts(q=0x1008)) == _lib.MOE_EALIGN
+    assert call(a=ctypes.c_void_p(0x1004)) == _lib.MOE_EALIGN
+    assert call(out=ctypes.c_void_p(0x1002)) == _lib.MOE_EALIGN
+
+
+@no_gpu
+def test_combine_argument_checks():
+    L = _lib.lib()
+    assert L.moe_combine(None, 8, FAKE, FAKE, 2, 2, 64, FAKE, None) == _lib.MOE_EINVAL
+    assert L.moe_combine(FAKE, 8, FAKE, FAKE, 2, 17, 64, FAKE, None) == _lib.MOE_EINVAL
+    assert L.moe_combine(FAKE, 8, FAKE, FAKE, 2, 2, 0, FAKE, None) == _lib.MOE_EINVAL
+    assert L.moe_combine(FAKE, 0, FAKE, FAKE, 2, 2, 64, FAKE, None) == _lib.MOE_EINVAL
+    assert L.moe_combine(ctypes.c_void_p(0x1002), 8, FAKE, FAKE, 2, 2, 64, FAKE, None) == _lib.MOE_EALIGN
