@@ -5,6 +5,7 @@
  *
  *   moe_route_topk  logits -> top-k expert ids + routing weights
  *   moe_bucket      ids    -> CSR of routed rows per expert with padded prefix bases
+ *   mx4_pack_experts  one-time repack of MXFP4 expert weights into the GPU's chunked layout
  *   mx4_moe_gemv    gate_up / down MXFP4 projection, few rows per expert (decode)
  *   mx4_moe_gemm    the same function on MFMA, many rows per expert (prefill)
  *   moe_combine     router-weighted sum of each token's expert rows, in slot order
@@ -49,7 +50,7 @@ typedef enum {
   MOE_EINVAL = 1,  /* NULL pointer, non-positive size, k outside [1, min(E, MOE_MAX_K)]          */
   MOE_ESHAPE = 2,  /* K % 32 != 0, odd N with SwiGLU, tile_m outside [1, MOE_MAX_TILE_M],
                       mpad_max smaller than moe_mpad_max(...), E above MOE_MAX_E            */
-  MOE_EALIGN = 3,  /* weight nibble plane not 16-byte aligned, activations/outputs not 4-byte  */
+  MOE_EALIGN = 3,  /* weights, activations or outputs not 16-byte aligned                      */
   MOE_ELAUNCH = 4  /* the HIP runtime reported an error when the kernel was enqueued          */
 } moe_status;
 
@@ -61,6 +62,7 @@ typedef enum {
 #define MOE_MAX_K 16        /* experts per token */
 #define MOE_MAX_E 1024      /* experts per layer */
 #define MOE_MAX_TILE_M 256  /* bucket padding granule */
+#define MOE_GEMV_MAX_K 16384 /* reduction length of mx4_moe_gemv (mx4_moe_gemm has no limit) */
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* moe_strerror(int status);
@@ -106,15 +108,26 @@ int moe_bucket(const int32_t* ids, int64_t T, int k, int E, int tile_m, int64_t 
 
 /*
  * A stack of E MXFP4 expert matrices W[e] of N rows by K columns ([mx4]).
- *   q     u8 [E][N][K/2]: e2m1 codes, two per byte; element 2i of a row is the LOW nibble of byte
- *         i, element 2i+1 the HIGH nibble. 16-byte aligned (every 32-element block is 16 bytes).
- *   s     u8 [E][N][K/32]: e8m0 exponent byte of each 32-element block.
- *   bias  f32 [E][N], or NULL for no bias.
- * Decoded element = e2m1(code) * 2^(s - 127) as an fp32 value (+-inf if it exceeds the fp32
- * range; NaN for s == 255), where e2m1 = {0, .5, 1, 1.5, 2, 3, 4, 6} with bit 3 the sign.
+ * Element values: decoded element = e2m1(code) * 2^(scale - 127) as an fp32 value (+-inf if it
+ * exceeds the fp32 range; NaN for scale byte 255), e2m1 = {0, .5, 1, 1.5, 2, 3, 4, 6} with bit 3
+ * the sign; element 2i of a row is the LOW nibble of byte i of the row, element 2i+1 the HIGH.
  * For the gate_up projection N = 2*ffn, rows [0, ffn) are the gate and rows [ffn, 2*ffn) the up
  * projection; for the down projection N = dim.
- * The descriptor itself is a HOST struct; q, s and bias are device pointers.
+ *
+ * Two byte layouts of the same stack (KB = K/32 blocks per row; a block = 16 nibble bytes +
+ * 1 scale byte):
+ *   checkpoint layout (row-major, as stored by gpt-oss checkpoints)
+ *     q [E][N][K/2] bytes, s [E][N][KB] bytes.
+ *   chunked layout (what the projections read): each expert's K is cut into chunks of 4 blocks,
+ *     C = ceil(KB/4) chunks, chunk c holding blocks [4c, 4c + w_c), w_c = min(4, KB - 4c), and
+ *     stored chunk after chunk, all N rows of a chunk together:
+ *       block (e, n, kb) is block number  e*N*KB + (kb/4)*N*4 + n*w_c + (kb%4)
+ *       its 16 nibble bytes at q + 16*number, its scale byte at s + number.
+ *     Same total size as the checkpoint layout. Every 16 consecutive rows of a chunk are one
+ *     contiguous run of 16*w_c*16 bytes, which is what one wavefront of the projection kernels
+ *     reads per load instruction.
+ * mx4_experts describes a stack in the CHUNKED layout. The descriptor itself is a HOST struct;
+ * q, s and bias are device pointers; bias is f32 [E][N] or NULL.
  */
 typedef struct {
   const uint8_t* q;
@@ -124,6 +137,16 @@ typedef struct {
   int N;
   int K;
 } mx4_experts;
+
+/*
+ * Repack an expert stack from the checkpoint layout to the chunked layout (a byte permutation,
+ * run once when the weights are loaded). q_src/s_src in the checkpoint layout, q_dst/s_dst
+ * receive the chunked layout; the buffers must not overlap. Sizes E*N*K/2 and E*N*K/32 bytes.
+ * Errors: MOE_EINVAL for NULL pointers or E/N < 1; MOE_ESHAPE for K < 32 or K % 32 != 0;
+ *         MOE_EALIGN for q_src or q_dst not 16-byte aligned; MOE_ELAUNCH.
+ */
+int mx4_pack_experts(const uint8_t* q_src, const uint8_t* s_src, int E, int N, int K,
+                     uint8_t* q_dst, uint8_t* s_dst, void* stream);
 
 /*
  * Routed-expert MXFP4 projection, bias-seeded, with an optional fused SwiGLU-OAI epilogue
@@ -148,9 +171,10 @@ typedef struct {
  * (prefill, tens to hundreds of rows per expert). Their results agree within fp32 summation
  * order, not bit-for-bit.
  * Errors: MOE_EINVAL for NULL a/w/q/s/counts/basep/out, a_rows < 1, E/N < 1, mpad_max < 1,
- *         unknown act; MOE_ESHAPE for K < 32 or K % 32 != 0, odd N with MOE_ACT_SWIGLU_OAI,
+ *         unknown act; MOE_ESHAPE for K < 32 or K % 32 != 0 (mx4_moe_gemv also for
+ *         K > MOE_GEMV_MAX_K), odd N with MOE_ACT_SWIGLU_OAI,
  *         tile_m outside [1, MOE_MAX_TILE_M], E > MOE_MAX_E, a_row == NULL with
- *         a_rows < mpad_max; MOE_EALIGN for q not 16-byte aligned or a/out not 4-byte aligned;
+ *         a_rows < mpad_max; MOE_EALIGN for q, a or out not 16-byte aligned;
  *         MOE_ELAUNCH if the runtime rejects the launch.
  */
 int mx4_moe_gemv(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const mx4_experts* w,

@@ -17,8 +17,8 @@ MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_ELAUNCH = 0, 1, 2, 3, 4
 MOE_ACT_NONE, MOE_ACT_SWIGLU_OAI = 0, 1
 MOE_MAX_K, MOE_MAX_E, MOE_MAX_TILE_M = 16, 1024, 256
 
-EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_moe_gemv",
-           "mx4_moe_gemm", "moe_combine")
+EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_pack_experts",
+           "mx4_moe_gemv", "mx4_moe_gemm", "moe_combine")
 
 
 class MoeError(RuntimeError):
@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route_topk.argtypes = [vp, i64, ci, ci, vp, vp, vp]
         L.moe_bucket.restype = ci
         L.moe_bucket.argtypes = [vp, i64, ci, ci, ci, i64, vp, vp, vp, vp, vp]
+        L.mx4_pack_experts.restype = ci
+        L.mx4_pack_experts.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp]
         proj = [vp, vp, i64, ctypes.POINTER(Mx4ExpertsC), vp, vp, ci, i64, ci, cf, cf, vp, vp]
         for name in ("mx4_moe_gemv", "mx4_moe_gemm"):
             getattr(L, name).restype = ci
@@ -108,10 +110,13 @@ def _call(fn: str, *args):
 
 
 class MX4Experts:
-    """A device-resident MXFP4 expert stack: q u8 [E][N][K/2], s u8 [E][N][K/32], bias f32 [E][N]
-    (or None). Holds the tensors alive and builds the C descriptor."""
+    """A device-resident MXFP4 expert stack in the chunked layout the projections read.
 
-    def __init__(self, q, s, bias=None):
+    Built from the checkpoint (row-major) layout — q u8 [E][N][K/2], s u8 [E][N][K/32] — with one
+    mx4_pack_experts call on the current stream; bias f32 [E][N] or None. Holds the tensors alive
+    and the C descriptor."""
+
+    def __init__(self, q, s, bias=None, stream=None):
         torch = _torch()
         _check(q, torch.uint8, "q")
         _check(s, torch.uint8, "s")
@@ -123,22 +128,44 @@ class MX4Experts:
             _check(bias, torch.float32, "bias")
             if tuple(bias.shape) != (E, N):
                 raise ValueError(f"bias: expected shape {(E, N)}")
-        self.q, self.s, self.bias = q, s, bias
+        qp = torch.empty_like(q)
+        sp = torch.empty_like(s)
+        _call("mx4_pack_experts", _ptr(q), _ptr(s), E, N, K, _ptr(qp), _ptr(sp), _stream(stream))
+        self.q, self.s, self.bias = qp, sp, bias
         self.E, self.N, self.K = E, N, K
-        self.c = Mx4ExpertsC(q.data_ptr(), s.data_ptr(),
+        self.c = Mx4ExpertsC(qp.data_ptr(), sp.data_ptr(),
                              None if bias is None else bias.data_ptr(), E, N, K)
 
     @classmethod
     def from_numpy(cls, d: dict, device="cuda"):
         torch = _torch()
-        q = torch.from_numpy(d["q"]).to(device)
-        s = torch.from_numpy(d["s"]).to(device)
-        b = None if d.get("bias") is None else torch.from_numpy(d["bias"]).to(device)
+        q = torch.from_numpy(np_contig(d["q"])).to(device)
+        s = torch.from_numpy(np_contig(d["s"])).to(device)
+        b = None if d.get("bias") is None else torch.from_numpy(np_contig(d["bias"])).to(device)
         return cls(q, s, b)
 
     @property
     def nbytes(self) -> int:
         return self.q.numel() + self.s.numel()
+
+
+def np_contig(a):
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    return a if a.flags.writeable else a.copy()
+
+
+def mx4_pack_experts(q, s, q_dst=None, s_dst=None, stream=None):
+    """Checkpoint-layout MXFP4 stack -> chunked layout (device tensors of the same shapes)."""
+    torch = _torch()
+    _check(q, torch.uint8, "q")
+    _check(s, torch.uint8, "s")
+    E, N, half_k = q.shape
+    q_dst = torch.empty_like(q) if q_dst is None else q_dst
+    s_dst = torch.empty_like(s) if s_dst is None else s_dst
+    _call("mx4_pack_experts", _ptr(q), _ptr(s), E, N, half_k * 2, _ptr(q_dst), _ptr(s_dst),
+          _stream(stream))
+    return q_dst, s_dst
 
 
 def moe_route_topk(logits, k: int, ids=None, w=None, stream=None):

@@ -2,10 +2,10 @@
 // Every check runs before anything is enqueued; on failure nothing is enqueued.
 #include "common.hpp"
 
-int moe_launch_gemv(const uint16_t* a, const int32_t* a_row, const mx4_experts* w,
+int moe_launch_gemv(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const mx4_experts* w,
                     const int32_t* counts, const int32_t* basep, int tile_m, int64_t mpad_max,
                     int act, float alpha, float limit, void* out, hipStream_t stream);
-int moe_launch_gemm(const uint16_t* a, const int32_t* a_row, const mx4_experts* w,
+int moe_launch_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const mx4_experts* w,
                     const int32_t* counts, const int32_t* basep, int tile_m, int64_t mpad_max,
                     int act, float alpha, float limit, void* out, hipStream_t stream);
 
@@ -46,7 +46,8 @@ extern "C" int mx4_moe_gemv(const uint16_t* a, const int32_t* a_row, int64_t a_r
                             void* out, void* stream) {
   const int st = check_projection(a, a_row, a_rows, w, counts, basep, tile_m, mpad_max, act, out);
   if (st != MOE_OK) return st;
-  return moe_launch_gemv(a, a_row, w, counts, basep, tile_m, mpad_max, act, alpha, limit, out,
+  if (a_rows > 0x7FFFFFFFLL || w->K > MOE_GEMV_MAX_K) return MOE_ESHAPE;
+  return moe_launch_gemv(a, a_row, a_rows, w, counts, basep, tile_m, mpad_max, act, alpha, limit, out,
                          (hipStream_t)stream);
 }
 
@@ -56,6 +57,6 @@ extern "C" int mx4_moe_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_r
                             void* out, void* stream) {
   const int st = check_projection(a, a_row, a_rows, w, counts, basep, tile_m, mpad_max, act, out);
   if (st != MOE_OK) return st;
-  return moe_launch_gemm(a, a_row, w, counts, basep, tile_m, mpad_max, act, alpha, limit, out,
+  return moe_launch_gemm(a, a_row, a_rows, w, counts, basep, tile_m, mpad_max, act, alpha, limit, out,
                          (hipStream_t)stream);
 }

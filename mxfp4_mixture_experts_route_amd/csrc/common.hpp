@@ -14,6 +14,37 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kChunkBlocks = 4;   // MX blocks per chunk of the chunked weight layout
+
+// Raw buffer resource over `bytes` bytes at p (gfx9 family: dword3 = 0x00020000, stride 0).
+// Buffer loads whose offset lands at or past `bytes` return zeros instead of touching memory,
+// which is how the kernels below handle tails and invalid lanes without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOOB = 0x80000000u;   // a buffer offset past every resource: loads give zero
+
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  u32x4_t out;
+  __builtin_memcpy(&out, &v, sizeof(out));
+  return out;
+}
+
+__device__ __forceinline__ uint32_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+
+// Block number of block kb of row n of expert e in the chunked MXFP4 layout: the expert's K is
+// cut into chunks of 4 blocks stored one after another, all N rows of a chunk together (the
+// last chunk may be narrower). Nibbles live at 16 * number, the scale byte at number.
+__host__ __device__ __forceinline__ size_t chunked_block(int e, int n, int kb, int N, int KB) {
+  const int c = kb / kChunkBlocks;
+  const int w = (KB - c * kChunkBlocks) < kChunkBlocks ? (KB - c * kChunkBlocks) : kChunkBlocks;
+  return (size_t)e * N * KB + (size_t)c * N * kChunkBlocks + (size_t)n * w + (kb % kChunkBlocks);
+}
 
 // e8m0 exponent byte -> the fp32 value 2^(e-127): e << 23 is the normal encoding for e >= 1,
 // e == 0 is the subnormal 2^-127 (0x00400000), and e == 255 is NaN.

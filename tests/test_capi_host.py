@@ -113,3 +113,13 @@ def test_combine_argument_checks():
     assert L.moe_combine(FAKE, 8, FAKE, FAKE, 2, 2, 0, FAKE, None) == _lib.MOE_EINVAL
     assert L.moe_combine(FAKE, 0, FAKE, FAKE, 2, 2, 64, FAKE, None) == _lib.MOE_EINVAL
     assert L.moe_combine(ctypes.c_void_p(0x1002), 8, FAKE, FAKE, 2, 2, 64, FAKE, None) == _lib.MOE_EALIGN
+
+
+@no_gpu
+def test_pack_argument_checks():
+    L = _lib.lib()
+    A = ctypes.c_void_p(0x1000)
+    assert L.mx4_pack_experts(None, FAKE, 2, 8, 64, A, FAKE, None) == _lib.MOE_EINVAL
+    assert L.mx4_pack_experts(A, FAKE, 0, 8, 64, A, FAKE, None) == _lib.MOE_EINVAL
+    assert L.mx4_pack_experts(A, FAKE, 2, 8, 48, A, FAKE, None) == _lib.MOE_ESHAPE
+    assert L.mx4_pack_experts(ctypes.c_void_p(0x1008), FAKE, 2, 8, 64, A, FAKE, None) == _lib.MOE_EALIGN

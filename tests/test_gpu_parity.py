@@ -64,6 +64,35 @@ MEDIUM = dict(seed=11, E=8, D=320, F=224, T=100, k=4, tile_m=16)
 
 
 # ---------------------------------------------------------------------------------------------
+# weight repack: a byte permutation, bit-exact against the layout's definition
+# ---------------------------------------------------------------------------------------------
+
+def chunked_reference(q, s):
+    """The chunked layout written out with numpy: per expert, chunk c (blocks 4c .. 4c+w_c-1) of
+    all N rows, row after row."""
+    E, N, half_k = q.shape
+    KB = half_k // 16
+    qb = q.reshape(E, N, KB, 16)
+    qo, so = [], []
+    for e in range(E):
+        for c0 in range(0, KB, 4):
+            w = min(4, KB - c0)
+            qo.append(qb[e, :, c0:c0 + w, :].reshape(-1))
+            so.append(s[e, :, c0:c0 + w].reshape(-1))
+    return np.concatenate(qo), np.concatenate(so)
+
+
+@pytest.mark.parametrize("E,N,K", [(3, 37, 160), (2, 16, 32), (4, 64, 2880), (1, 5, 96)])
+def test_pack_matches_layout_definition(E, N, K):
+    W = synth.random_mx4(E * N + K, E, N, K)
+    log(f"pack E={E} N={N} K={K}")
+    qp, sp = moe.mx4_pack_experts(dev(W["q"]), dev(W["s"]))
+    q_ref, s_ref = chunked_reference(W["q"], W["s"])
+    assert np.array_equal(host(qp).reshape(-1), q_ref)
+    assert np.array_equal(host(sp).reshape(-1), s_ref)
+
+
+# ---------------------------------------------------------------------------------------------
 # routing and bucketing: bit-exact
 # ---------------------------------------------------------------------------------------------
 
