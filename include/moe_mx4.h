@@ -63,6 +63,7 @@ typedef enum {
 #define MOE_MAX_E 1024      /* experts per layer */
 #define MOE_MAX_TILE_M 256  /* bucket padding granule */
 #define MOE_GEMV_MAX_K 16384 /* reduction length of mx4_moe_gemv (mx4_moe_gemm has no limit) */
+#define MOE_SCALE_ROW_ALIGN 16 /* bytes: scale rows of the chunked layout are padded to this */
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* moe_strerror(int status);
@@ -118,14 +119,15 @@ int moe_bucket(const int32_t* ids, int64_t T, int k, int E, int tile_m, int64_t 
  * 1 scale byte):
  *   checkpoint layout (row-major, as stored by gpt-oss checkpoints)
  *     q [E][N][K/2] bytes, s [E][N][KB] bytes.
- *   chunked layout (what the projections read): each expert's K is cut into chunks of 4 blocks,
- *     C = ceil(KB/4) chunks, chunk c holding blocks [4c, 4c + w_c), w_c = min(4, KB - 4c), and
- *     stored chunk after chunk, all N rows of a chunk together:
- *       block (e, n, kb) is block number  e*N*KB + (kb/4)*N*4 + n*w_c + (kb%4)
- *       its 16 nibble bytes at q + 16*number, its scale byte at s + number.
- *     Same total size as the checkpoint layout. Every 16 consecutive rows of a chunk are one
- *     contiguous run of 16*w_c*16 bytes, which is what one wavefront of the projection kernels
- *     reads per load instruction.
+ *   chunked layout (what the projections read):
+ *     nibbles: each expert's K is cut into chunks of 4 blocks, C = ceil(KB/4) chunks, chunk c
+ *       holding blocks [4c, 4c + w_c), w_c = min(4, KB - 4c), stored chunk after chunk with all
+ *       N rows of a chunk together: the 16 nibble bytes of block (e, n, kb) start at byte
+ *       16 * (e*N*KB + (kb/4)*N*4 + n*w_c + (kb%4)). Same size as the checkpoint's q. Every
+ *       16 consecutive rows of a chunk are one contiguous run of 16*w_c*16 bytes, which is what
+ *       one wavefront of the projection kernels reads per load instruction.
+ *     scales: row-major with every row padded to SP = roundup(KB, 16) bytes (padding bytes 0):
+ *       the scale of block (e, n, kb) is byte (e*N + n)*SP + kb. Size E*N*SP bytes.
  * mx4_experts describes a stack in the CHUNKED layout. The descriptor itself is a HOST struct;
  * q, s and bias are device pointers; bias is f32 [E][N] or NULL.
  */
@@ -139,11 +141,12 @@ typedef struct {
 } mx4_experts;
 
 /*
- * Repack an expert stack from the checkpoint layout to the chunked layout (a byte permutation,
- * run once when the weights are loaded). q_src/s_src in the checkpoint layout, q_dst/s_dst
- * receive the chunked layout; the buffers must not overlap. Sizes E*N*K/2 and E*N*K/32 bytes.
+ * Repack an expert stack from the checkpoint layout to the chunked layout (a byte permutation
+ * plus the scale-row padding, run once when the weights are loaded). q_src/s_src in the
+ * checkpoint layout (E*N*K/2 and E*N*K/32 bytes); q_dst (E*N*K/2 bytes) and s_dst
+ * (E*N*roundup(K/32, 16) bytes) receive the chunked layout; no buffer may overlap another.
  * Errors: MOE_EINVAL for NULL pointers or E/N < 1; MOE_ESHAPE for K < 32 or K % 32 != 0;
- *         MOE_EALIGN for q_src or q_dst not 16-byte aligned; MOE_ELAUNCH.
+ *         MOE_EALIGN for q_src, q_dst or s_dst not 16-byte aligned; MOE_ELAUNCH.
  */
 int mx4_pack_experts(const uint8_t* q_src, const uint8_t* s_src, int E, int N, int K,
                      uint8_t* q_dst, uint8_t* s_dst, void* stream);

@@ -129,7 +129,7 @@ class MX4Experts:
             if tuple(bias.shape) != (E, N):
                 raise ValueError(f"bias: expected shape {(E, N)}")
         qp = torch.empty_like(q)
-        sp = torch.empty_like(s)
+        sp = torch.empty((E, N, scale_row_bytes(K)), dtype=torch.uint8, device=q.device)
         _call("mx4_pack_experts", _ptr(q), _ptr(s), E, N, K, _ptr(qp), _ptr(sp), _stream(stream))
         self.q, self.s, self.bias = qp, sp, bias
         self.E, self.N, self.K = E, N, K
@@ -155,14 +155,20 @@ def np_contig(a):
     return a if a.flags.writeable else a.copy()
 
 
+def scale_row_bytes(K: int) -> int:
+    """Bytes per scale row in the chunked layout: K/32 padded to a multiple of 16."""
+    return (K // 32 + 15) // 16 * 16
+
+
 def mx4_pack_experts(q, s, q_dst=None, s_dst=None, stream=None):
-    """Checkpoint-layout MXFP4 stack -> chunked layout (device tensors of the same shapes)."""
+    """Checkpoint-layout MXFP4 stack -> chunked layout: q_dst like q, s_dst u8 [E][N][SP]."""
     torch = _torch()
     _check(q, torch.uint8, "q")
     _check(s, torch.uint8, "s")
     E, N, half_k = q.shape
     q_dst = torch.empty_like(q) if q_dst is None else q_dst
-    s_dst = torch.empty_like(s) if s_dst is None else s_dst
+    if s_dst is None:
+        s_dst = torch.empty((E, N, scale_row_bytes(half_k * 2)), dtype=torch.uint8, device=q.device)
     _call("mx4_pack_experts", _ptr(q), _ptr(s), E, N, half_k * 2, _ptr(q_dst), _ptr(s_dst),
           _stream(stream))
     return q_dst, s_dst

@@ -39,20 +39,21 @@ __device__ __forceinline__ uint32_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t
 
 // Block number of block kb of row n of expert e in the chunked MXFP4 layout: the expert's K is
 // cut into chunks of 4 blocks stored one after another, all N rows of a chunk together (the
-// last chunk may be narrower). Nibbles live at 16 * number, the scale byte at number.
+// last chunk may be narrower). Its 16 nibble bytes start at byte 16 * number.
 __host__ __device__ __forceinline__ size_t chunked_block(int e, int n, int kb, int N, int KB) {
   const int c = kb / kChunkBlocks;
   const int w = (KB - c * kChunkBlocks) < kChunkBlocks ? (KB - c * kChunkBlocks) : kChunkBlocks;
   return (size_t)e * N * KB + (size_t)c * N * kChunkBlocks + (size_t)n * w + (kb % kChunkBlocks);
 }
 
-// e8m0 exponent byte -> the fp32 value 2^(e-127): e << 23 is the normal encoding for e >= 1,
-// e == 0 is the subnormal 2^-127 (0x00400000), and e == 255 is NaN.
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  uint32_t bits = e ? (e << 23) : 0x00400000u;
-  bits = (e == 255u) ? 0x7FC00000u : bits;
-  return __uint_as_float(bits);
-}
+// Bytes per scale row of the chunked layout: the row's KB scale bytes padded to 16.
+__host__ __device__ __forceinline__ int scale_row_bytes(int KB) { return (KB + 15) & ~15; }
+
+// Scale operand of v_cvt_scalef32_* for an e8m0 byte e: the byte in the fp32 exponent field.
+// The instruction reads only that field and decodes it as e8m0 itself: 2^(e-127), with e = 0
+// giving 2^-127 (subnormal results kept) and e = 255 giving NaN; checked on gfx950 against the
+// explicit decode for every (scale byte, code byte) pair, and end to end by the one-hot sweep.
+__device__ __forceinline__ float e8m0_scale_operand(uint32_t e) { return __uint_as_float(e << 23); }
 
 // float -> bf16 bit pattern, round to nearest even (NaN -> quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {

@@ -64,7 +64,7 @@ struct GemmCtx {
   float alpha, limit;
   int tile_base[kGmWT];
   int rows_in[kGmWT];
-  uint32_t wo[kGmWT], wol[kGmWT], so[kGmWT], sol[kGmWT];
+  uint32_t wo[kGmWT], wol[kGmWT], so[kGmWT];
 };
 
 // One pass with NTT live token tiles (compile-time, so the MFMA loop is straight-line code and
@@ -79,12 +79,12 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint16_t* __restrict
   auto load_w = [&](int c, u32x4_t (&dq)[kGmWT], uint32_t (&dx)[kGmWT]) {
     if (c < C) {
       const uint32_t cq = (uint32_t)c * g.N * (kChunkBlocks * 16);
-      const uint32_t cs = (uint32_t)c * g.N * kChunkBlocks;
+      const uint32_t cs = (uint32_t)c * kChunkBlocks;   // scale byte of block 4c + lg
       const bool last = (c == C - 1);
 #pragma unroll
       for (int t = 0; t < kGmWT; ++t) {
         dq[t] = buf_load16(g.rq, last ? g.wol[t] : g.wo[t], cq);
-        dx[t] = buf_load8(g.rs, last ? g.sol[t] : g.so[t], cs);
+        dx[t] = buf_load8(g.rs, g.so[t], cs);
       }
     } else {
 #pragma unroll
@@ -161,7 +161,7 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint16_t* __restrict
 #pragma unroll
         for (int t = 0; t < kGmWT; ++t) {
           cq[t] = wq[pf][t];
-          cs[t] = e8m0_to_f32(wx[pf][t]);
+          cs[t] = e8m0_scale_operand(wx[pf][t]);
         }
         load_w(c + kGmPF, wq[pf], wx[pf]);   // refill this ring slot (zeros past K)
         const uint16_t* xb = xs + (pf & 1) * kGmBufElems;   // c0 is even: c & 1 == pf & 1
@@ -276,8 +276,9 @@ gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
 
   // buffer resources: this expert's nibbles and scales, and the activation rows
   const size_t ebase = (size_t)e * N * KB;   // first block of this expert (chunked layout)
+  const int SP = scale_row_bytes(KB);        // scale row pitch (padding reads as 0)
   g.rq = make_rsrc(q + 16 * ebase, (uint32_t)N * KB * 16);
-  g.rs = make_rsrc(s + ebase, (uint32_t)N * KB);
+  g.rs = make_rsrc(s + (size_t)e * N * SP, (uint32_t)N * SP);
   g.ra = make_rsrc(a, (uint32_t)a_rows * K * 2);
 
   // per-lane offsets of the lane's block in a full chunk and in the (narrower) last chunk
@@ -285,10 +286,9 @@ gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
   for (int t = 0; t < kGmWT; ++t) {
     const uint32_t n = (uint32_t)(g.tile_base[t] + g.lr);
     const bool ok = g.lr < g.rows_in[t];
-    g.so[t] = ok ? n * kChunkBlocks + g.lg : kOOB;
-    g.sol[t] = (ok && g.lg < wlast) ? n * wlast + g.lg : kOOB;
-    g.wo[t] = ok ? g.so[t] * 16 : kOOB;
-    g.wol[t] = (ok && g.lg < wlast) ? g.sol[t] * 16 : kOOB;
+    g.so[t] = ok ? n * SP + g.lg : kOOB;
+    g.wo[t] = ok ? (n * kChunkBlocks + g.lg) * 16 : kOOB;
+    g.wol[t] = (ok && g.lg < wlast) ? (n * wlast + g.lg) * 16 : kOOB;
   }
 
   for (int p0 = 0; p0 < cnt; p0 += kGmTT * 16) {

@@ -13,9 +13,14 @@
 //  * Weights are in the chunked layout (chunks of 4 MX blocks, all rows of a chunk together). A
 //    wavefront owns 16 weight rows: lane (r = lane%16, g = lane/16) takes block g of every chunk
 //    of row r, so each load instruction of the wavefront reads one contiguous 1 KB run.
-//  * The wavefront finds its expert by itself (one load of counts[], a ballot) and then issues the
-//    loads of its first 16 chunks at once (256 B per lane); each ring slot is refilled with the
-//    chunk 16 ahead as soon as it is consumed, so a launch waits for HBM latency about once.
+//  * The wavefront finds its expert by itself (one load of counts[], a ballot) and then issues
+//    every load of a K segment of up to 24 chunks at once (384 B of nibbles per lane; all of K
+//    at gpt-oss shapes), scales first and nibbles in K order. Loads complete in issue order, so
+//    chunk i is computed as soon as its own bytes arrive and the compute overlaps the stream.
+//    A lane's scale for chunk c is byte g of dword c of its (16-byte padded) scale row, so 6
+//    dwordx4 loads carry the scales of 24 chunks.
+//  * All global loads are buffer loads with per-lane offsets computed once; lanes with nothing to
+//    load point past the resource and read zeros.
 //  * When every activation row fits (decode: a_rows * K * 2 bytes <= 24 KB) the workgroup stages
 //    them all into LDS at kernel start, independently of the CSR; otherwise it stages the
 //    expert's rows per pass of up to 4 rows.
@@ -31,21 +36,22 @@
 namespace moe {
 
 constexpr int kGvMaxRB = 4;       // activation rows per pass (per-expert staging)
-constexpr int kGvRing = 16;       // chunk loads in flight per lane (a ring refilled as it drains)
+constexpr int kGvSeg = 24;        // chunks per K segment, all in flight at once (K <= 3072: one)
 constexpr int kGvPitch = 80;      // LDS bytes per staged 32-element block (64 used)
 constexpr int kGvLdsBudget = 65536;
 constexpr int kGvMaxStage = 6;    // 16-byte pieces per thread when all activation rows are staged
 constexpr int kGvMaxThreads = 256;
 
-// Expert of this wavefront's slot: the slot-th expert with a non-zero count, or -1. One load of
-// counts[] per 64 experts and a ballot; no LDS, no barrier.
+// Expert of this wavefront's slot: the slot-th expert with a non-zero count, or -1. c64 is this
+// lane's counts[lane] (0 past E), loaded by the caller before anything else; experts past 64
+// are scanned 64 at a time. No LDS, no barrier.
 __device__ __forceinline__ int wave_slot_expert(const int32_t* __restrict__ counts, int E,
-                                                int slot) {
+                                                int slot, int c64) {
   const int lane = (int)(threadIdx.x & 63);
   int seen = 0;
   for (int base = 0; base < E; base += 64) {
     const int e = base + lane;
-    const bool live = (e < E) && (counts[e] > 0);
+    const bool live = base == 0 ? (c64 > 0) : ((e < E) && (counts[e] > 0));
     uint64_t ballot = __ballot(live);
     const int n = __popcll(ballot);
     if (slot < seen + n) {
@@ -73,7 +79,10 @@ gemv_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
   const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, lg = lane >> 4;
   const int F = N >> 1;
 
-  // 1. activations that do not depend on the CSR: issue their loads first
+  // Vector loads complete in issue order, so they are issued in the order they are needed:
+  // counts (expert lookup), the activations, the bias, then the weights.
+  // 1. counts for the expert lookup, then the activations that do not depend on the CSR
+  const int c64 = (lane < E) ? counts[lane] : 0;
   const int all_pieces = stage_all ? a_rows * KB * 4 : 0;
   uint4 stage[kGvMaxStage];
 #pragma unroll
@@ -85,7 +94,7 @@ gemv_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
   }
 
   // 2. expert of this workgroup's slot (each wavefront on its own)
-  const int e = wave_slot_expert(counts, E, (int)blockIdx.y);
+  const int e = wave_slot_expert(counts, E, (int)blockIdx.y, c64);
   if (e < 0) return;  // uniform over the workgroup: fewer live experts than slots
 
   // 3. this wavefront's 16 weight rows
@@ -100,30 +109,48 @@ gemv_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
     n = unit * 16 + lr;
     valid = n < N;
   }
-  const size_t ebase = (size_t)e * N * KB;
-  auto load_chunk = [&](int c, u32x4_t& wq, uint32_t& ex) {
-    const int kb = c * kChunkBlocks + lg;
-    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    uint32_t x = 127u;
-    if (valid && c < C && kb < KB) {
-      const int w = min(kChunkBlocks, KB - c * kChunkBlocks);
-      const size_t blk = ebase + (size_t)c * N * kChunkBlocks + (size_t)n * w + lg;
-      v = *reinterpret_cast<const u32x4_t*>(q + 16 * blk);
-      x = s[blk];
-    }
-    wq = v;
-    ex = x;
+  const int SP = scale_row_bytes(KB);
+  const int wlast = KB - (C - 1) * kChunkBlocks;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + 16 * (size_t)e * N * KB, (uint32_t)N * KB * 16);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s + (size_t)e * N * SP, (uint32_t)N * SP);
+  const uint32_t wo = valid ? ((uint32_t)n * kChunkBlocks + lg) * 16 : kOOB;       // full chunk
+  const uint32_t wol = (valid && lg < wlast) ? ((uint32_t)n * wlast + lg) * 16 : kOOB;  // last
+  const uint32_t so = valid ? (uint32_t)n * SP : kOOB;
+  // branch-free: a chunk past K gets an out-of-range offset and reads zeros
+  auto load_chunk = [&](int c, u32x4_t& wq) {
+    const uint32_t off = (c < C - 1) ? wo : (c == C - 1 ? wol : kOOB);
+    wq = buf_load16(rq, off, (uint32_t)c * N * (kChunkBlocks * 16));
   };
-  u32x4_t wq[kGvRing];
-  uint32_t ex[kGvRing];
+  // one K segment in K order: for every 4 chunks, their scale dwords, then their nibbles. The
+  // scheduling barriers keep that issue order (the compiler would otherwise move the scale
+  // loads last, and chunk 0 would then wait for the whole segment).
+  u32x4_t wq[kGvSeg];
+  uint32_t sc[kGvSeg];
+  auto load_segment = [&](int c0) {
 #pragma unroll
-  for (int i = 0; i < kGvRing; ++i) load_chunk(i, wq[i], ex[i]);
+    for (int i = 0; i < kGvSeg / 4; ++i) {
+      // 16 scale bytes = 4 chunks; a group past the padded scale row reads zeros (it would
+      // otherwise read the next row's scales, where a NaN byte would poison 0 * scale)
+      const uint32_t g_off = (uint32_t)(c0 + 4 * i) * 4;
+      const u32x4_t v = buf_load16(rs, g_off < (uint32_t)SP ? so : kOOB, g_off);
+      sc[4 * i + 0] = v[0];
+      sc[4 * i + 1] = v[1];
+      sc[4 * i + 2] = v[2];
+      sc[4 * i + 3] = v[3];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) load_chunk(c0 + 4 * i + k, wq[4 * i + k]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const float b0 = (valid && bias && lg == 0) ? bias[(size_t)e * N + n] : 0.0f;
+  load_segment(0);
 
   const int cnt = counts[e];
   const int row0 = basep[e];
-  const float b0 = (valid && bias && lg == 0) ? bias[(size_t)e * N + n] : 0.0f;
 
-  // 4. activations staged up front go to LDS
+  // 4. activations staged up front go to LDS, followed by one all-zero block
+  const size_t zero_blk = (size_t)(stage_all ? a_rows : rb) * KB;
+  if (tid < 4) *reinterpret_cast<uint4*>(xs + zero_blk * kGvPitch + tid * 16) = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
   for (int i = 0; i < kGvMaxStage; ++i) {
     const int p = tid + i * nthreads;
@@ -133,10 +160,7 @@ gemv_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
 
   for (int p0 = 0; p0 < cnt; p0 += rb) {
     const int nr = min(rb, cnt - p0);
-    if (p0 > 0) {   // another pass over the same rows (more than rb rows): refill the ring
-#pragma unroll
-      for (int i = 0; i < kGvRing; ++i) load_chunk(i, wq[i], ex[i]);
-    }
+
     if (!stage_all) {
       __syncthreads();  // the previous pass is done with xs
       for (int p = tid; p < nr * KB * 4; p += nthreads) {
@@ -160,42 +184,41 @@ gemv_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
 #pragma unroll
     for (int rr = 0; rr < kGvMaxRB; ++rr) acc[rr] = b0;  // bias-seeded accumulator
 
-    for (int c0 = 0; c0 < C; c0 += kGvRing) {
+    for (int c0 = 0; c0 < C; c0 += kGvSeg) {
+      if (c0 > 0 || p0 > 0) load_segment(c0);   // later segments / passes (K > 3072, > rb rows)
 #pragma unroll
-      for (int i = 0; i < kGvRing; ++i) {
-        const int c = c0 + i;
-        const int kb = c * kChunkBlocks + lg;
-        if (c < C) {
-          if (kb < KB) {
-            const float sc = e8m0_to_f32(ex[i]);
-            bf16x2_t wv[16];
+      for (int i = 0; i < kGvSeg; ++i) {
+        // straight-line over the segment (no branches, so each chunk waits only for its own
+        // loads): blocks past K read zero weights and the block's x is clamped, then dropped
+        const int kb = (c0 + i) * kChunkBlocks + lg;
+        const bool in_k = kb < KB;
+        {
+          const float scl = e8m0_scale_operand(__builtin_amdgcn_ubfe(sc[i], 8 * lg, 8));
+          bf16x2_t wv[16];
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              wv[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wq[i][d], sc, 0);
-              wv[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wq[i][d], sc, 1);
-              wv[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wq[i][d], sc, 2);
-              wv[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wq[i][d], sc, 3);
-            }
+          for (int d = 0; d < 4; ++d) {
+            wv[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wq[i][d], scl, 0);
+            wv[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wq[i][d], scl, 1);
+            wv[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wq[i][d], scl, 2);
+            wv[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wq[i][d], scl, 3);
+          }
 #pragma unroll
-            for (int rr = 0; rr < kGvMaxRB; ++rr) {
-              if (rr < nr) {
-                const uint8_t* xp = xs + ((size_t)xrow[rr] * KB + kb) * kGvPitch;
-                float part = 0.0f;
+          for (int rr = 0; rr < kGvMaxRB; ++rr) {
+            if (rr < nr) {
+              // blocks past K (zero weights) read the zero block instead of activations
+              const uint8_t* xp = xs + (in_k ? (size_t)xrow[rr] * KB + kb : zero_blk) * kGvPitch;
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                  const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xp + 16 * d);
+              for (int d = 0; d < 4; ++d) {
+                const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xp + 16 * d);
 #pragma unroll
-                  for (int bb = 0; bb < 4; ++bb) {
-                    const uint32_t xw = xv[bb];
-                    part = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * d + bb], as_bf16x2(xw), part,
-                                                           false);
-                  }
+                for (int bb = 0; bb < 4; ++bb) {
+                  const uint32_t xw = xv[bb];
+                  acc[rr] = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * d + bb], as_bf16x2(xw),
+                                                            acc[rr], false);
                 }
-                acc[rr] += part;
               }
             }
           }
-          load_chunk(c + kGvRing, wq[i], ex[i]);   // refill the slot (no load past K)
         }
       }
     }
@@ -237,10 +260,10 @@ int moe_launch_gemv(const uint16_t* a, const int32_t* a_row, int64_t a_rows, con
   const int threads = 64 * waves;
   const int stage_all =
       ((int64_t)a_rows * KB * 4 <= (int64_t)moe::kGvMaxStage * threads) ? 1 : 0;
-  int rb = (int)(moe::kGvLdsBudget / row_lds);
+  int rb = (int)((moe::kGvLdsBudget - moe::kGvPitch) / row_lds);   // rows + the zero block
   if (rb > moe::kGvMaxRB) rb = moe::kGvMaxRB;
   if (rb < 1) return MOE_ESHAPE;
-  const size_t lds = stage_all ? (size_t)a_rows * row_lds : (size_t)rb * row_lds;
+  const size_t lds = (stage_all ? (size_t)a_rows * row_lds : (size_t)rb * row_lds) + moe::kGvPitch;
   const int64_t bx = (units + waves - 1) / waves;
   if (act == MOE_ACT_SWIGLU_OAI)
     hipLaunchKernelGGL(moe::gemv_kernel<MOE_ACT_SWIGLU_OAI>, dim3((unsigned)bx, (unsigned)slots),

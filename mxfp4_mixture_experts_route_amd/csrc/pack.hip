@@ -1,8 +1,8 @@
 // mx4_pack_experts: checkpoint (row-major) MXFP4 layout -> chunked layout read by the projections.
 //
 // A pure byte permutation, run once when weights are loaded: one thread per 16-byte MX block,
-// reading the source in order (coalesced) and writing the block and its scale byte to their
-// chunked positions. The chunked layout makes each wavefront load of the projection kernels one
+// reading the source in order (coalesced) and writing the block to its chunked position and its
+// scale byte to the padded scale row. The chunked layout makes each wavefront load of the projection kernels one
 // contiguous 1 KB run and keeps all workgroups of a launch inside a compact window of memory.
 #include "common.hpp"
 
@@ -14,6 +14,7 @@ __global__ void __launch_bounds__(kPackThreads)
 pack_kernel(const uint8_t* __restrict__ q_src, const uint8_t* __restrict__ s_src, int E, int N,
             int KB, uint8_t* __restrict__ q_dst, uint8_t* __restrict__ s_dst) {
   const size_t total = (size_t)E * N * KB;
+  const int SP = scale_row_bytes(KB);
   for (size_t i = (size_t)blockIdx.x * kPackThreads + threadIdx.x; i < total;
        i += (size_t)gridDim.x * kPackThreads) {
     const int kb = (int)(i % KB);
@@ -22,7 +23,10 @@ pack_kernel(const uint8_t* __restrict__ q_src, const uint8_t* __restrict__ s_src
     const int e = (int)(row / N);
     const size_t d = chunked_block(e, n, kb, N, KB);
     *reinterpret_cast<uint4*>(q_dst + 16 * d) = *reinterpret_cast<const uint4*>(q_src + 16 * i);
-    s_dst[d] = s_src[i];
+    uint8_t* srow = s_dst + row * SP;
+    srow[kb] = s_src[i];
+    if (kb == KB - 1)
+      for (int p = KB; p < SP; ++p) srow[p] = 0;   // padding of the scale row
   }
 }
 
@@ -32,7 +36,8 @@ extern "C" int mx4_pack_experts(const uint8_t* q_src, const uint8_t* s_src, int 
                                 uint8_t* q_dst, uint8_t* s_dst, void* stream) {
   if (!q_src || !s_src || !q_dst || !s_dst || E < 1 || N < 1) return MOE_EINVAL;
   if (K < 32 || (K % 32) != 0) return MOE_ESHAPE;
-  if ((((uintptr_t)q_src) & 15) || (((uintptr_t)q_dst) & 15)) return MOE_EALIGN;
+  if ((((uintptr_t)q_src) & 15) || (((uintptr_t)q_dst) & 15) || (((uintptr_t)s_dst) & 15))
+    return MOE_EALIGN;
   const size_t total = (size_t)E * N * (K / 32);
   size_t blocks = (total + moe::kPackThreads - 1) / moe::kPackThreads;
   if (blocks > 65536) blocks = 65536;

@@ -123,3 +123,4 @@ def test_pack_argument_checks():
     assert L.mx4_pack_experts(A, FAKE, 0, 8, 64, A, FAKE, None) == _lib.MOE_EINVAL
     assert L.mx4_pack_experts(A, FAKE, 2, 8, 48, A, FAKE, None) == _lib.MOE_ESHAPE
     assert L.mx4_pack_experts(ctypes.c_void_p(0x1008), FAKE, 2, 8, 64, A, FAKE, None) == _lib.MOE_EALIGN
+    assert L.mx4_pack_experts(A, FAKE, 2, 8, 64, A, ctypes.c_void_p(0x2001), None) == _lib.MOE_EALIGN

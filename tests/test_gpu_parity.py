@@ -68,18 +68,21 @@ MEDIUM = dict(seed=11, E=8, D=320, F=224, T=100, k=4, tile_m=16)
 # ---------------------------------------------------------------------------------------------
 
 def chunked_reference(q, s):
-    """The chunked layout written out with numpy: per expert, chunk c (blocks 4c .. 4c+w_c-1) of
-    all N rows, row after row."""
+    """The chunked layout written out with numpy: nibbles per expert chunk by chunk (blocks
+    4c .. 4c+w_c-1 of all N rows, row after row); scales row-major, each row zero-padded to a
+    multiple of 16 bytes."""
     E, N, half_k = q.shape
     KB = half_k // 16
     qb = q.reshape(E, N, KB, 16)
-    qo, so = [], []
+    qo = []
     for e in range(E):
         for c0 in range(0, KB, 4):
             w = min(4, KB - c0)
             qo.append(qb[e, :, c0:c0 + w, :].reshape(-1))
-            so.append(s[e, :, c0:c0 + w].reshape(-1))
-    return np.concatenate(qo), np.concatenate(so)
+    SP = (KB + 15) // 16 * 16
+    so = np.zeros((E, N, SP), dtype=np.uint8)
+    so[:, :, :KB] = s
+    return np.concatenate(qo), so.reshape(-1)
 
 
 @pytest.mark.parametrize("E,N,K", [(3, 37, 160), (2, 16, 32), (4, 64, 2880), (1, 5, 96)])
