@@ -37,6 +37,10 @@ __device__ __forceinline__ uint32_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n (<= 63) vector-memory
+// operations of this wavefront are outstanding, and for nothing else.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // Block number of block kb of row n of expert e in the chunked MXFP4 layout: the expert's K is
 // cut into chunks of 4 blocks stored one after another, all N rows of a chunk together (the
 // last chunk may be narrower). Its 16 nibble bytes start at byte 16 * number.
@@ -54,6 +58,16 @@ __host__ __device__ __forceinline__ int scale_row_bytes(int KB) { return (KB + 1
 // giving 2^-127 (subnormal results kept) and e = 255 giving NaN; checked on gfx950 against the
 // explicit decode for every (scale byte, code byte) pair, and end to end by the one-hot sweep.
 __device__ __forceinline__ float e8m0_scale_operand(uint32_t e) { return __uint_as_float(e << 23); }
+
+// 8 e2m1 codes (one dword of an MX block: elements 8t..8t+7, element 2b in the low nibble of
+// byte b) -> 8 bf16 scaled by the block's e8m0 scale operand; exact.
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t w8, float scale) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w8, scale, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w8, scale, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w8, scale, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w8, scale, 3);
+  return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
 
 // float -> bf16 bit pattern, round to nearest even (NaN -> quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {

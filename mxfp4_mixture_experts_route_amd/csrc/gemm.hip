@@ -45,14 +45,6 @@ constexpr int kGmPitch = kGmChunkK + 8;  // bf16 per LDS row (272 B: rows 4 bank
 constexpr int kGmBufElems = kGmTT * 16 * kGmPitch;
 constexpr int kGmLdsBytes = 2 * kGmBufElems * 2;
 
-__device__ __forceinline__ bf16x8_t dequant8(uint32_t w8, float scale) {
-  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w8, scale, 0);
-  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w8, scale, 1);
-  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w8, scale, 2);
-  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w8, scale, 3);
-  return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
 // Everything one pass over up to 16*NTT routed rows of one expert needs.
 struct GemmCtx {
   const int32_t* a_row;
