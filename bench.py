@@ -5,13 +5,16 @@ A step is one pass of the whole chain (route -> bucket -> gate_up + SwiGLU-OAI -
 combine) over one batch. The headline workload is gpt-oss-20b-shaped decode: E=32 experts,
 dim = ffn = 2880, top-4, one token, through 24 distinct seeded MoE layers (10.15 GB of MXFP4
 experts resident in HBM, 1.27 GB touched per step, far more than the 256 MB last-level cache), so a
-step is one decode token through the model's 24 MoE layers, replayed as one HIP graph.
+step is one decode token through the model's 24 MoE layers, replayed as one HIP graph. Each layer
+runs as mx4_moe_decode (the chain fused into two launches); the five-call chain (route, bucket,
+GEMV, GEMV, combine) is timed beside it.
 
 Prints ONE JSON line. `value` = decode tokens/s through the 24-layer stack. The same line also
-carries the dominant kernel's roofline (its average duration from HIP events recorded around
-each launch on the stream it runs on), the decode weight GB/s of the two MXFP4 GEMVs, the pp512
-prefill expert-GEMM TFLOP/s (gpt-oss-20b shape, T=512, bf16 MFMA), and the CPU oracle timed on a
-bounded sample of the decode workload on the host cores.
+carries the dominant kernel's roofline, the decode weight GB/s of the two MXFP4 projections, the
+pp512 prefill expert-GEMM TFLOP/s (gpt-oss-20b shape, T=512, bf16 MFMA), and the CPU oracle timed
+on a bounded sample of the decode workload on the host cores. Kernel durations come from the
+library's kernel timing (moe_timing_arm: HIP events the runtime stamps at each kernel's own start
+and end, on the stream it runs on), the interval a rocprofv3 kernel trace reports.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
 """
@@ -33,7 +36,7 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--kernel-reps", type=int, default=4, help="passes of per-launch event timing")
+    p.add_argument("--kernel-reps", type=int, default=4, help="passes of per-kernel timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=12.0)
@@ -93,6 +96,13 @@ class Layer:
         self.down()
         self.combine()
 
+    def decode(self):
+        """The chain as mx4_moe_decode (two launches; h in routed-row order, T*k rows)."""
+        c = self.csr
+        self.moe.mx4_moe_decode(self.logits, self.x, self.GU, self.DN, self.wl.k, 1.702, 7.0,
+                                out={"ids": self.ids, "w": self.w, "counts": c[0], "basep": c[1],
+                                     "row_tok": c[2], "pos": c[3], "h": self.h, "y": self.y})
+
 
 def build_layers(moe, synth, torch, wl, kernel, n_layers):
     out = []
@@ -139,26 +149,29 @@ def graph_time(torch, fn, steps, warmup):
     return time.perf_counter() - t0, g
 
 
-def kernel_times_us(torch, layers, stages, reps, sleep_cycles):
-    """Average duration (us) of each stage's kernel from HIP events recorded around every launch
-    on the launching stream. A sleep kernel first keeps the GPU busy so the host can queue the
-    launches ahead of it (no host-submission gaps inside the event pairs)."""
-    ev = {name: [] for name in stages}
+def kernel_times_us(moe, torch, layers, call, launches, reps, sleep_cycles):
+    """Average kernel duration (us) of each of the `launches` kernels that call(L) makes per
+    layer, from the library's kernel timing (events stamped at each kernel's own start and end).
+    Layers are queued back to back behind a sleep kernel, in batches that fit MOE_TIMING_MAX."""
+    per_batch = max(1, 64 // launches)
+    sums = [0.0] * launches
+    n = 0
     for _ in range(reps):
-        torch.cuda.synchronize()
-        if sleep_cycles:
-            torch.cuda._sleep(sleep_cycles)
-        for L in layers:
-            L.route_bucket()
-            for name in stages:
-                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                s.record()
-                getattr(L, name)()
-                e.record()
-                ev[name].append((s, e))
-            L.combine()
-    torch.cuda.synchronize()
-    return {name: 1000.0 * sum(s.elapsed_time(e) for s, e in v) / len(v) for name, v in ev.items()}
+        for b0 in range(0, len(layers), per_batch):
+            batch = layers[b0:b0 + per_batch]
+            torch.cuda.synchronize()
+            if sleep_cycles:
+                torch.cuda._sleep(sleep_cycles)
+            moe.moe_timing_arm(len(batch) * launches)
+            for L in batch:
+                call(L)
+            ms = moe.moe_timing_read(len(batch) * launches)
+            moe.moe_timing_arm(0)
+            for i in range(len(batch)):
+                for j in range(launches):
+                    sums[j] += ms[i * launches + j]
+            n += len(batch)
+    return [1000.0 * v / n for v in sums]
 
 
 def touched_experts(torch, layers):
@@ -208,22 +221,27 @@ def main():
     wl = synth.WORKLOADS["decode_t1"]
     log(f"building {wl.layers} layers of {wl.desc}")
     layers = build_layers(moe, synth, torch, wl, "gemv", wl.layers)
-    step = lambda: [L.chain() for L in layers]   # noqa: E731
-    log(f"timing {args.steps} graph-replayed steps after {args.warmup} warmup")
-    secs, _ = graph_time(torch, step, args.steps, args.warmup)
+    log(f"timing {args.steps} graph-replayed steps after {args.warmup} warmup (fused decode)")
+    secs, _ = graph_time(torch, lambda: [L.decode() for L in layers], args.steps, args.warmup)
     ms_per_step = 1000.0 * secs / args.steps
     tokens_per_s = wl.T * args.steps / secs
+    log("the same steps as the five-call chain")
+    secs5, _ = graph_time(torch, lambda: [L.chain() for L in layers], args.steps, args.warmup)
 
-    log("per-launch kernel timing (HIP events)")
-    kt = kernel_times_us(torch, layers, ("gate_up", "down"), args.kernel_reps, sleep_cycles)
+    log("kernel timing")
+    fused_us = kernel_times_us(moe, torch, layers, lambda L: L.decode(), 2, args.kernel_reps,
+                               sleep_cycles)
+    chain_us = kernel_times_us(moe, torch, layers, lambda L: L.chain(), 5, args.kernel_reps,
+                               sleep_cycles)
     n_touch = touched_experts(torch, layers)
     per_expert_gu = 2 * wl.ffn * wl.dim * 17 // 32          # nibbles + scales, bytes
     per_expert_dn = wl.dim * wl.ffn * 17 // 32
     avg_touch = sum(n_touch) / len(n_touch)
     gu_bytes = avg_touch * per_expert_gu
     dn_bytes = avg_touch * per_expert_dn
-    gu_gbps = gu_bytes / (kt["gate_up"] * 1e3)
-    wgbps = (gu_bytes + dn_bytes) / ((kt["gate_up"] + kt["down"]) * 1e3)
+    gu_gbps = gu_bytes / (fused_us[0] * 1e3)
+    fused_gbps = (gu_bytes + dn_bytes) / ((fused_us[0] + fused_us[1]) * 1e3)
+    gemv_gbps = (gu_bytes + dn_bytes) / ((chain_us[2] + chain_us[3]) * 1e3)
 
     result = {
         "metric": "MoE chain tokens/s; decode mx4 weight GB/s; pp512 expert GEMM TFLOP/s (1 GPU)",
@@ -240,17 +258,26 @@ def main():
         "data": "synthetic",
         "config": {"workload": "gpt-oss-20b-shaped decode, T=1, 24 distinct MoE layers per step",
                    "E": wl.E, "dim": wl.dim, "ffn": wl.ffn, "k": wl.k, "T": wl.T,
-                   "layers": wl.layers, "tile_m": wl.tile_m, "weights": "mxfp4",
-                   "accumulate": "f32", "projection": "mx4_moe_gemv", "graph": "hip graph replay"},
-        "roofline": {"kernel": "mx4_moe_gemv gate_up + SwiGLU-OAI", "bound": "hbm",
-                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(kt["gate_up"], 3)},
-        "decode": {"weight_GBps_gemv_pair": round(wgbps, 1),
-                   "frac_hbm_peak": round(wgbps / HBM_PEAK_GBPS, 4),
-                   "gate_up_us": round(kt["gate_up"], 3), "down_us": round(kt["down"], 3),
-                   "touched_experts_per_layer": avg_touch,
-                   "per_layer_chain_us": round(ms_per_step * 1000.0 / wl.layers, 3)},
+                   "layers": wl.layers, "weights": "mxfp4", "accumulate": "f32",
+                   "chain": "mx4_moe_decode (2 launches per layer)", "graph": "hip graph replay"},
+        "roofline": {"kernel": "decode_gate_up_kernel (routing + gate_up + SwiGLU-OAI)",
+                     "bound": "hbm", "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(fused_us[0], 3)},
+        "decode": {"fused": {"gate_up_kernel_us": round(fused_us[0], 3),
+                             "down_combine_kernel_us": round(fused_us[1], 3),
+                             "weight_GBps": round(fused_gbps, 1),
+                             "frac_hbm_peak": round(fused_gbps / HBM_PEAK_GBPS, 4),
+                             "per_layer_us": round(ms_per_step * 1000.0 / wl.layers, 3)},
+                   "five_call_chain": {"tokens_per_s": round(wl.T * args.steps / secs5, 2),
+                                       "per_layer_us": round(1e6 * secs5 / (args.steps * wl.layers), 3),
+                                       "route_us": round(chain_us[0], 3),
+                                       "bucket_us": round(chain_us[1], 3),
+                                       "gemv_gate_up_us": round(chain_us[2], 3),
+                                       "gemv_down_us": round(chain_us[3], 3),
+                                       "combine_us": round(chain_us[4], 3),
+                                       "gemv_weight_GBps": round(gemv_gbps, 1)},
+                   "touched_experts_per_layer": avg_touch},
     }
     del layers
     torch.cuda.empty_cache()
@@ -263,7 +290,9 @@ def main():
         psecs, _ = graph_time(torch, lambda: [L.chain() for L in players], max(5, args.steps // 5),
                               args.warmup)
         p_steps = max(5, args.steps // 5)
-        pkt = kernel_times_us(torch, players, ("gate_up", "down"), args.kernel_reps, sleep_cycles)
+        pkt = kernel_times_us(moe, torch, players, lambda L: L.chain(), 5, args.kernel_reps,
+                              sleep_cycles)
+        pkt = {"gate_up": pkt[2], "down": pkt[3]}
         R = pw.T * pw.k
         flops = 2.0 * R * pw.dim * 3 * pw.ffn
         tflops = flops / ((pkt["gate_up"] + pkt["down"]) * 1e-6) / 1e12

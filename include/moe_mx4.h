@@ -10,6 +10,10 @@
  *   mx4_moe_gemm    the same function on MFMA, many rows per expert (prefill)
  *   moe_combine     router-weighted sum of each token's expert rows, in slot order
  *
+ * and, for decode (a few tokens), the same chain fused into two launches:
+ *
+ *   mx4_moe_decode  logits + x -> routing, CSR, h, (d), y
+ *
  * Sources (web pages on the daScript repository's dasLLAMA engine; cited by tag below):
  *   [fusion]  PR #3579 "dasLLAMA gpt-oss arc", commit log, the Metal fusion-lane commit: the
  *             bucket pass computes each expert's padded-prefix base inside its workgroup and
@@ -168,11 +172,12 @@ int mx4_pack_experts(const uint8_t* q_src, const uint8_t* s_src, int E, int N, i
  *             NULL for the down step, whose input rows are already in CSR order). Every live
  *             row's a_row entry must be in [0, a_rows); with a_row == NULL a_rows >= mpad_max.
  *   counts, basep: from moe_bucket (same E, tile_m, mpad_max).
- * mx4_moe_gemv and mx4_moe_gemm compute the same function with different kernels: the GEMV
- * streams each weight byte once through the VALU (decode, a handful of rows per expert), the
- * GEMM dequantizes MXFP4 to bf16 in registers and runs bf16 MFMA with fp32 accumulation
- * (prefill, tens to hundreds of rows per expert). Their results agree within fp32 summation
- * order, not bit-for-bit.
+ * mx4_moe_gemv and mx4_moe_gemm compute the same function with different kernels, both
+ * dequantizing MXFP4 to bf16 in registers for bf16 MFMA with fp32 accumulation: the GEMV keeps
+ * a whole K segment of each wavefront's weights in flight and takes up to 16 routed rows per
+ * pass (decode, a handful of rows per expert), the GEMM runs over all of an expert's rows per
+ * workgroup in 16-row tiles (prefill, tens to hundreds of rows per expert). Their results agree
+ * within fp32 summation order, not bit-for-bit.
  * Errors: MOE_EINVAL for NULL a/w/q/s/counts/basep/out, a_rows < 1, E/N < 1, mpad_max < 1,
  *         unknown act; MOE_ESHAPE for K < 32 or K % 32 != 0 (mx4_moe_gemv also for
  *         K > MOE_GEMV_MAX_K), odd N with MOE_ACT_SWIGLU_OAI,
@@ -188,6 +193,39 @@ int mx4_moe_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const 
                  const int32_t* counts, const int32_t* basep, int tile_m, int64_t mpad_max,
                  int act, float alpha, float limit, void* out, void* stream);
 
+#define MOE_DECODE_MAX_T 16  /* tokens per mx4_moe_decode call */
+#define MOE_DECODE_MAX_K 8   /* experts per token in mx4_moe_decode */
+
+/*
+ * The whole routed chain of a few tokens in two launches ([chain]: stage 1 = gate and up rows +
+ * bias + activation, stage 2 = down rows + bias and the routing-weighted sum in slot order;
+ * [fusion]: bias-seeded accumulators, per-expert padded-prefix bases). Computes exactly what
+ * moe_route_topk, moe_bucket (tile_m = 1), mx4_moe_gemv with MOE_ACT_SWIGLU_OAI, mx4_moe_gemv
+ * with MOE_ACT_NONE and moe_combine compute, except that h and d are indexed by ROUTED ROW
+ * rho = t*k + s (token t, slot s) instead of by CSR row:
+ *   ids, w      i32/f32 [T][k]  routing (as moe_route_topk)
+ *   counts [E], basep [E+1], row_tok [T*k], pos [T][k]: the CSR with tile_m = 1 (as moe_bucket;
+ *               mpad = T*k, no padding rows)
+ *   h     bf16 [T*k][F]  h[rho] = SwiGLU-OAI(gate_up projection of x[t] by expert ids[t][s])
+ *   d     f32  [T*k][D]  d[rho] = down projection of h[rho] by that expert, bias included; may be
+ *                        NULL (then never written: the combine happens on chip)
+ *   y     f32  [T][D]    y[t][n] = sum over s in slot order of w[t][s] * d[t*k+s][n]
+ *   logits f32 [T][E], x bf16 [T][D]; w_gu: E experts of [2F][D] (gate rows [0,F), up rows
+ *   [F,2F)), w_dn: E experts of [D][F], both in the chunked layout of mx4_pack_experts.
+ * Each pick streams its expert's weights once, so an expert picked by several of the T tokens
+ * is read several times: for more than a few tokens the CSR calls are the cheaper path.
+ * Errors: MOE_EINVAL for NULL pointers (other than d), T < 1, E < 1, k < 1, k > min(E,
+ *         MOE_MAX_K); MOE_ESHAPE for T > MOE_DECODE_MAX_T, k > MOE_DECODE_MAX_K, E > MOE_MAX_E,
+ *         w_gu / w_dn with another E, D or F not a positive multiple of 32, w_dn not [D][F],
+ *         activation rows too long for LDS (k*F*2 bytes above ~55 KB); MOE_EALIGN for x, h or the
+ *         weight arrays not 16-byte aligned, logits, d or y not 4-byte aligned; MOE_ELAUNCH if
+ *         the runtime rejects a launch.
+ */
+int mx4_moe_decode(const float* logits, const uint16_t* x, int64_t T, int E, int k,
+                   const mx4_experts* w_gu, const mx4_experts* w_dn, float alpha, float limit,
+                   int32_t* ids, float* w, int32_t* counts, int32_t* basep, int32_t* row_tok,
+                   int32_t* pos, uint16_t* h, float* d, float* y, void* stream);
+
 /*
  * Router-weighted combine ([chain]: routing-weighted sum of the expert rows in slot order).
  *   y[t][n] = sum_{s=0..k-1} w[t][s] * d[pos[t][s]][n], accumulated in fp32 in slot order.
@@ -200,6 +238,24 @@ int mx4_moe_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const 
  */
 int moe_combine(const float* d, int64_t d_rows, const int32_t* pos, const float* w, int64_t T,
                 int k, int D, float* y, void* stream);
+
+#define MOE_TIMING_MAX 64   /* launches one moe_timing_arm can time */
+
+/*
+ * Kernel timing, for measurement. After moe_timing_arm(n), the next n kernel launches made by
+ * any call of this library (in launch order, on whatever stream) are launched with a pair of
+ * HIP events that the runtime stamps at the kernel's own start and end (hipExtLaunchKernel),
+ * i.e. the kernel execution interval a kernel trace reports, without the dispatch gaps around
+ * it. moe_timing_read(ms, n) waits for the first n timed launches since the arm and writes
+ * their durations in milliseconds. moe_timing_arm(0) disarms. The event pairs are created on
+ * the current device at the first arm and kept until the process ends (the one exception to
+ * "keeps no state"). Not thread-safe; never arm while a stream is being captured into a graph.
+ * Errors: MOE_EINVAL for n outside [0, MOE_TIMING_MAX] or ms == NULL; MOE_ESHAPE for reading
+ *         more launches than were timed; MOE_ELAUNCH if the runtime fails to create or read an
+ *         event.
+ */
+int moe_timing_arm(int n);
+int moe_timing_read(float* ms, int n);
 
 #ifdef __cplusplus
 }

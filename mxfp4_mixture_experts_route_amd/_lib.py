@@ -18,7 +18,8 @@ MOE_ACT_NONE, MOE_ACT_SWIGLU_OAI = 0, 1
 MOE_MAX_K, MOE_MAX_E, MOE_MAX_TILE_M = 16, 1024, 256
 
 EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_pack_experts",
-           "mx4_moe_gemv", "mx4_moe_gemm", "moe_combine")
+           "mx4_moe_gemv", "mx4_moe_gemm", "moe_combine", "mx4_moe_decode", "moe_timing_arm",
+           "moe_timing_read")
 
 
 class MoeError(RuntimeError):
@@ -60,6 +61,14 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).argtypes = proj
         L.moe_combine.restype = ci
         L.moe_combine.argtypes = [vp, i64, vp, vp, i64, ci, ci, vp, vp]
+        L.moe_timing_arm.restype = ci
+        L.moe_timing_arm.argtypes = [ci]
+        L.moe_timing_read.restype = ci
+        L.moe_timing_read.argtypes = [ctypes.POINTER(ctypes.c_float), ci]
+        pe = ctypes.POINTER(Mx4ExpertsC)
+        L.mx4_moe_decode.restype = ci
+        L.mx4_moe_decode.argtypes = [vp, vp, i64, ci, ci, pe, pe, cf, cf,
+                                     vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -246,6 +255,47 @@ def moe_combine(d, pos, w, out=None, stream=None):
     _call("moe_combine", _ptr(d), d.shape[0], _ptr(pos), _ptr(w), T, k, D, _ptr(y),
           _stream(stream))
     return y
+
+
+def mx4_moe_decode(logits, x, gate_up: MX4Experts, down: MX4Experts, k: int,
+                   alpha: float = 1.702, limit: float = 7.0, want_d: bool = False, out=None,
+                   stream=None):
+    """Fused decode chain of a few tokens (two launches). Returns a dict with ids, w, counts,
+    basep, row_tok, pos (CSR with tile_m = 1), h [T*k][F] and d [T*k][D] in routed-row order
+    (d only with want_d), and y [T][D]. `out` may hold preallocated tensors under those keys."""
+    torch = _torch()
+    _check(logits, torch.float32, "logits")
+    _check(x, torch.bfloat16, "x")
+    T, E = logits.shape
+    D, F = gate_up.K, gate_up.N // 2
+    dev = logits.device
+    o = dict(out or {})
+    shapes = {"ids": ((T, k), torch.int32), "w": ((T, k), torch.float32),
+              "counts": ((E,), torch.int32), "basep": ((E + 1,), torch.int32),
+              "row_tok": ((T * k,), torch.int32), "pos": ((T, k), torch.int32),
+              "h": ((T * k, F), torch.bfloat16), "y": ((T, D), torch.float32)}
+    if want_d:
+        shapes["d"] = ((T * k, D), torch.float32)
+    for key, (shape, dt) in shapes.items():
+        if key not in o:
+            o[key] = torch.empty(shape, dtype=dt, device=dev)
+    _call("mx4_moe_decode", _ptr(logits), _ptr(x), T, E, k, ctypes.byref(gate_up.c),
+          ctypes.byref(down.c), float(alpha), float(limit), _ptr(o["ids"]), _ptr(o["w"]),
+          _ptr(o["counts"]), _ptr(o["basep"]), _ptr(o["row_tok"]), _ptr(o["pos"]), _ptr(o["h"]),
+          _ptr(o.get("d")), _ptr(o["y"]), _stream(stream))
+    return o
+
+
+def moe_timing_arm(n: int) -> None:
+    """Time the library's next n kernel launches (kernel execution only); 0 disarms."""
+    _call("moe_timing_arm", int(n))
+
+
+def moe_timing_read(n: int) -> list:
+    """Durations in ms of the first n launches timed since moe_timing_arm (waits for them)."""
+    buf = (ctypes.c_float * max(1, n))()
+    _call("moe_timing_read", buf, int(n))
+    return [float(buf[i]) for i in range(n)]
 
 
 def moe_layer(x, logits, gate_up: MX4Experts, down: MX4Experts, k: int, tile_m: int,

@@ -7,6 +7,7 @@
 // sums the padded counts of the experts below its own to get basep[e], then compacts its rows in
 // ascending token order with wavefront ballots (an ordered scan, so the result is unique).
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace moe {
 
@@ -107,7 +108,7 @@ extern "C" int moe_bucket(const int32_t* ids, int64_t T, int k, int E, int tile_
   if (E > MOE_MAX_E || tile_m < 1 || tile_m > MOE_MAX_TILE_M) return MOE_ESHAPE;
   const int64_t need = moe_mpad_max(T, k, E, tile_m);
   if (mpad_max < need || mpad_max > 0x7FFFFFFFLL) return MOE_ESHAPE;
-  hipLaunchKernelGGL(moe::bucket_kernel, dim3((unsigned)E), dim3(moe::kBucketThreads), 0,
+  moe::launch(moe::bucket_kernel, dim3((unsigned)E), dim3(moe::kBucketThreads), 0,
                      (hipStream_t)stream, ids, T, k, E, tile_m, mpad_max, counts, basep, row_tok,
                      pos);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;

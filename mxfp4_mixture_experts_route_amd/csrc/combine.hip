@@ -5,6 +5,7 @@
 // routing-weighted sum in slot order. y[t][n] = sum_s w[t][s] * d[pos[t][s]][n], fp32, s = 0..k-1.
 // One thread per 4 consecutive outputs; each d row segment is read with 16-byte loads.
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace moe {
 
@@ -56,7 +57,7 @@ extern "C" int moe_combine(const float* d, int64_t d_rows, const int32_t* pos, c
   if (blocks > 0x7FFFFFFF) return MOE_ESHAPE;
   // 16-byte vector access when every row starts 16-byte aligned; otherwise the scalar path
   const int vec = ((D & 3) == 0) && !(((uintptr_t)d) & 15) && !(((uintptr_t)y) & 15);
-  hipLaunchKernelGGL(moe::combine_kernel, dim3((unsigned)blocks), dim3(moe::kCombineThreads), 0,
+  moe::launch(moe::combine_kernel, dim3((unsigned)blocks), dim3(moe::kCombineThreads), 0,
                      (hipStream_t)stream, d, d_rows, pos, w, T, k, D, y, vec);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

@@ -33,6 +33,7 @@
 //  * SwiGLU mode pairs gate tiles with the matching up tiles in the same wavefront, so the
 //    epilogue is register-local and only bf16 h leaves the kernel.
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace moe {
 
@@ -322,11 +323,11 @@ int moe_launch_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, con
     lds_attr_set = true;
   }
   if (act == MOE_ACT_SWIGLU_OAI)
-    hipLaunchKernelGGL(moe::gemm_kernel<MOE_ACT_SWIGLU_OAI>, dim3((unsigned)bx, (unsigned)slots),
+    moe::launch(moe::gemm_kernel<MOE_ACT_SWIGLU_OAI>, dim3((unsigned)bx, (unsigned)slots),
                        dim3(moe::kGmThreads), moe::kGmLdsBytes, stream, a, a_row, (int)a_rows,
                        w->q, w->s, w->bias, counts, basep, w->E, w->N, w->K, alpha, limit, out);
   else
-    hipLaunchKernelGGL(moe::gemm_kernel<MOE_ACT_NONE>, dim3((unsigned)bx, (unsigned)slots),
+    moe::launch(moe::gemm_kernel<MOE_ACT_NONE>, dim3((unsigned)bx, (unsigned)slots),
                        dim3(moe::kGmThreads), moe::kGmLdsBytes, stream, a, a_row, (int)a_rows,
                        w->q, w->s, w->bias, counts, basep, w->E, w->N, w->K, alpha, limit, out);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;

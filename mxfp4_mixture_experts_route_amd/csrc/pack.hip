@@ -5,6 +5,7 @@
 // scale byte to the padded scale row. The chunked layout makes each wavefront load of the projection kernels one
 // contiguous 1 KB run and keeps all workgroups of a launch inside a compact window of memory.
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace moe {
 
@@ -41,7 +42,7 @@ extern "C" int mx4_pack_experts(const uint8_t* q_src, const uint8_t* s_src, int 
   const size_t total = (size_t)E * N * (K / 32);
   size_t blocks = (total + moe::kPackThreads - 1) / moe::kPackThreads;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(moe::pack_kernel, dim3((unsigned)blocks), dim3(moe::kPackThreads), 0,
+  moe::launch(moe::pack_kernel, dim3((unsigned)blocks), dim3(moe::kPackThreads), 0,
                      (hipStream_t)stream, q_src, s_src, E, N, K / 32, q_dst, s_dst);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

@@ -1,0 +1,133 @@
+// Top-k expert selection of one token by one wavefront (shared by moe_route_topk and the fused
+// decode layer).
+//
+// A token picks its k largest router logits, in descending order, equal logits ordered by
+// ascending expert id; its routing weights are the softmax over the k selected logits, computed
+// in double relative to the largest and rounded to f32 (gpt-oss router). The per-token expert
+// ids, and k = 4 at gpt-oss shape, come from PR #3579 "dasLLAMA gpt-oss arc" (fused MoE expert
+// chain commit) and PR #3558 (section "gpt-oss: mx4 kernels to the lab-winning shape").
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kRoutePerLane = MOE_MAX_E / kWave;     // logits held per lane
+
+// a ranks before b: larger value; ties -> lower id. -0.0 == +0.0 as floats.
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+  return (va > vb) || (va == vb && ia < ib);
+}
+
+// Logits of one row for wave_topk_select: lane l holds experts j*64 + l (0 past E).
+__device__ __forceinline__ void wave_topk_load(const float* __restrict__ row, int E,
+                                               float (&v)[kRoutePerLane]) {
+  const int lane = (int)(threadIdx.x & 63);
+#pragma unroll
+  for (int j = 0; j < kRoutePerLane; ++j) {
+    const int e = j * kWave + lane;
+    v[j] = (e < E) ? row[e] : 0.0f;
+  }
+}
+
+// The k best experts of one logits row (E <= MOE_MAX_E, k <= min(E, MOE_MAX_K)) held as by
+// wave_topk_load. Lane r < k ends with the r-th pick in (my_id, my_v); other lanes' outputs are
+// unspecified. k rounds of a wavefront arg-best over per-lane candidates; no LDS.
+__device__ __forceinline__ void wave_topk_select(const float (&v)[kRoutePerLane], int E, int k,
+                                                 int& my_id, float& my_v) {
+  const int lane = (int)(threadIdx.x & 63);
+  uint32_t taken = 0;                 // bit j: expert j*64+lane already chosen (or absent)
+#pragma unroll
+  for (int j = 0; j < kRoutePerLane; ++j)
+    if (j * kWave + lane >= E) taken |= 1u << j;
+
+  my_id = 0;
+  my_v = 0.0f;
+  for (int r = 0; r < k; ++r) {
+    // this lane's best remaining candidate
+    float bv = 0.0f;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < kRoutePerLane; ++j) {
+      const int e = j * kWave + lane;
+      if (!(taken & (1u << j)) && (bi == 0x7FFFFFFF || ranks_before(v[j], e, bv, bi))) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+    // wavefront arg-best (lanes without a candidate carry id INT_MAX and never win)
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(bv, m);
+      const int oi = __shfl_xor(bi, m);
+      if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ranks_before(ov, oi, bv, bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == r) {
+      my_id = bi;
+      my_v = bv;
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+  }
+}
+
+// E <= 64: lane e holds logit e (v, loaded by the caller; anything for lanes >= E). Each lane
+// counts the logits that rank before its own (a broadcast of every lane's value through
+// v_readlane, no LDS and no dependent shuffle chains); the lane of rank r is pick r. Returns
+// this lane's rank (E or more for lanes >= E).
+__device__ __forceinline__ int wave_rank_small(float v, int E) {
+  const int lane = (int)(threadIdx.x & 63);
+  int rank = 0;
+  for (int j = 0; j < E; ++j) {
+    const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
+    rank += ranks_before(vj, j, v, lane) ? 1 : 0;
+  }
+  return lane < E ? rank : E + lane;
+}
+
+// Expert of pick `slot` from wave_rank_small ranks (uniform).
+__device__ __forceinline__ int rank_pick(int rank, int slot) {
+  return __ffsll((unsigned long long)__ballot(rank == slot)) - 1;
+}
+
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int& my_id,
+                                          float& my_v) {
+  if (E <= kWave) {
+    const int lane = (int)(threadIdx.x & 63);
+    const float v = lane < E ? row[lane] : 0.0f;
+    const int rank = wave_rank_small(v, E);
+    my_id = 0;
+    my_v = 0.0f;
+    for (int r = 0; r < k; ++r) {
+      const int id = rank_pick(rank, r);
+      const float vr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), id));
+      if (lane == r) {
+        my_id = id;
+        my_v = vr;
+      }
+    }
+    return;
+  }
+  float v[kRoutePerLane];
+  wave_topk_load(row, E, v);
+  wave_topk_select(v, E, k, my_id, my_v);
+}
+
+// Routing weights of the picks held by lanes 0..k-1 (wave_topk): lane 0 sums exp(v_r - v_0) in
+// double in pick order, then writes ids[r] and w[r] = f32(exp(v_r - v_0) / sum) for r < k.
+// Every lane must call it (it shuffles).
+__device__ __forceinline__ void write_topk(int my_id, float my_v, int k, int32_t* __restrict__ ids,
+                                           float* __restrict__ w) {
+  const int lane = (int)(threadIdx.x & 63);
+  const float v0 = __shfl(my_v, 0);
+  double den = 0.0;
+  for (int r = 0; r < k; ++r) den += exp((double)__shfl(my_v, r) - (double)v0);
+  if (lane < k) {
+    ids[lane] = my_id;
+    w[lane] = (float)(exp((double)my_v - (double)v0) / den);
+  }
+}
+
+}  // namespace moe

@@ -124,3 +124,46 @@ def test_pack_argument_checks():
     assert L.mx4_pack_experts(A, FAKE, 2, 8, 48, A, FAKE, None) == _lib.MOE_ESHAPE
     assert L.mx4_pack_experts(ctypes.c_void_p(0x1008), FAKE, 2, 8, 64, A, FAKE, None) == _lib.MOE_EALIGN
     assert L.mx4_pack_experts(A, FAKE, 2, 8, 64, A, ctypes.c_void_p(0x2001), None) == _lib.MOE_EALIGN
+
+
+@no_gpu
+def test_decode_argument_checks():
+    f = _lib.lib().mx4_moe_decode
+    gu, dn = experts(E=4, N=128, K=64), experts(E=4, N=64, K=64)
+
+    def call(logits=FAKE, x=FAKE, T=2, E=4, k=2, w_gu=gu, w_dn=dn, h=FAKE, d=FAKE, y=FAKE):
+        return f(logits, x, T, E, k, None if w_gu is None else ctypes.byref(w_gu),
+                 None if w_dn is None else ctypes.byref(w_dn), 1.702, 7.0,
+                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, h, d, y, None)
+
+    assert call(logits=None) == _lib.MOE_EINVAL
+    assert call(w_gu=None) == _lib.MOE_EINVAL
+    assert call(h=None) == _lib.MOE_EINVAL
+    assert call(y=None) == _lib.MOE_EINVAL
+    assert call(T=0) == _lib.MOE_EINVAL
+    assert call(k=0) == _lib.MOE_EINVAL
+    assert call(k=5) == _lib.MOE_EINVAL                         # k > E
+    assert call(T=17) == _lib.MOE_ESHAPE                        # T > MOE_DECODE_MAX_T
+    assert call(E=16, k=9, w_gu=experts(E=16, N=128, K=64),
+                w_dn=experts(E=16, N=64, K=64)) == _lib.MOE_ESHAPE   # k > MOE_DECODE_MAX_K
+    assert call(w_dn=experts(E=3, N=64, K=64)) == _lib.MOE_ESHAPE     # E mismatch
+    assert call(w_dn=experts(E=4, N=32, K=64)) == _lib.MOE_ESHAPE     # down not [D][F]
+    assert call(w_gu=experts(E=4, N=96, K=64), w_dn=experts(E=4, N=64, K=48)) == _lib.MOE_ESHAPE
+    assert call(w_gu=experts(E=4, N=127, K=64)) == _lib.MOE_ESHAPE    # odd N
+    assert call(x=ctypes.c_void_p(0x1008)) == _lib.MOE_EALIGN
+    assert call(h=ctypes.c_void_p(0x1004)) == _lib.MOE_EALIGN
+    assert call(y=ctypes.c_void_p(0x1002)) == _lib.MOE_EALIGN
+    assert call(d=ctypes.c_void_p(0x1001)) == _lib.MOE_EALIGN
+    assert call(d=None, y=ctypes.c_void_p(0x1002)) == _lib.MOE_EALIGN  # d may be NULL
+
+
+def test_timing_argument_checks():
+    L = _lib.lib()
+    assert L.moe_timing_arm(-1) == _lib.MOE_EINVAL
+    assert L.moe_timing_arm(65) == _lib.MOE_EINVAL
+    assert L.moe_timing_arm(0) == _lib.MOE_OK                # disarming needs no device
+    buf = (ctypes.c_float * 4)()
+    assert L.moe_timing_read(None, 1) == _lib.MOE_EINVAL
+    assert L.moe_timing_read(buf, -1) == _lib.MOE_EINVAL
+    assert L.moe_timing_read(buf, 1) == _lib.MOE_ESHAPE       # nothing was timed
+    assert L.moe_timing_read(buf, 0) == _lib.MOE_OK
