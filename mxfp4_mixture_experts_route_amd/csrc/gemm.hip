@@ -25,26 +25,43 @@
 //    16-byte block (lanes 16g..16g+15 take block g of a 4-block chunk), and the 4 k-substeps of
 //    the chunk take its 4 dwords; the activations are read from LDS in the same k order, and a
 //    sum over k does not depend on that order beyond fp32 rounding.
-//  * A ring of 4 chunks of weights (16 KB per wavefront) is in flight ahead of the MFMAs.
-//  * Activation rows are gathered through a_row (row_tok) into LDS, 128 k per chunk, double
-//    buffered; every B fragment read from LDS feeds 4 MFMAs (the wavefront's 4 weight tiles).
+//  * The K loop is a software pipeline: chunk c + 3 of the activations is copied into LDS by
+//    LDS-DMA buffer loads (no registers) at the start of iteration c, and chunk c + 4 of the
+//    weights is loaded into the register ring slot that chunk c has just used, at its end, so
+//    the slot is refilled in place (no register copies across the loop, whose waits would drain
+//    the pipeline). Vector loads complete in issue order and every iteration issues the same
+//    loads (chunks past K re-read the last one; their compute is skipped), so one wait for
+//    "everything but the last two iterations' loads and one weight chunk" at the top of
+//    iteration c covers both the weights and the activations of chunk c. A barrier per chunk
+//    publishes the activation chunk to all wavefronts and frees the LDS buffer (of 4) that the
+//    iteration's DMA overwrites.
+//  * Activation rows are gathered through a_row (row_tok) by the DMA, 128 k (256 B) per row
+//    per chunk, into an XOR-swizzled LDS layout (16-byte piece q of row m at slot q ^ (m % 16)),
+//    so the B-fragment reads of 16 consecutive rows hit 16 different bank groups; every B
+//    fragment feeds 4 MFMAs (the wavefront's 4 weight tiles).
 //  * Accumulators start at the bias of their weight row. Token tiles past the expert's count are
 //    never computed; rows past the count are never stored. Experts with no rows exit at once.
 //  * SwiGLU mode pairs gate tiles with the matching up tiles in the same wavefront, so the
 //    epilogue is register-local and only bf16 h leaves the kernel.
-#include "common.hpp"
+#include "gemv_core.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
-constexpr int kGmThreads = 256;          // 4 wavefronts
-constexpr int kGmWT = 4;                 // weight tiles (16 rows each) per wavefront
+constexpr int kGmWaves = 8;              // 2 wavefronts per SIMD
+constexpr int kGmThreads = 64 * kGmWaves;
+constexpr int kGmWT = 2;                 // weight tiles (16 rows each) per wavefront
 constexpr int kGmTT = 8;                 // token tiles (16 rows each) per pass: 128 routed rows
 constexpr int kGmChunkK = 128;           // k per chunk = 4 MX blocks
-constexpr int kGmPF = 4;                 // weight chunks in flight per wavefront
-constexpr int kGmPitch = kGmChunkK + 8;  // bf16 per LDS row (272 B: rows 4 banks apart)
-constexpr int kGmBufElems = kGmTT * 16 * kGmPitch;
-constexpr int kGmLdsBytes = 2 * kGmBufElems * 2;
+constexpr int kGmRowBytes = kGmChunkK * 2;   // activation bytes per row per chunk
+
+constexpr int kGmWRing = 4;              // weight chunks in flight (register ring slots)
+constexpr int kGmXRing = 4;              // activation chunk buffers in LDS (3 chunks ahead)
+// LDS of a pass with NTT token tiles
+__host__ __device__ constexpr int gemm_buf_bytes(int ntt) { return ntt * 16 * kGmRowBytes; }
+// after the activation ring: 1 KB that the DMA of wavefronts without a share of a chunk writes
+constexpr int kGmDummyOff = kGmXRing * gemm_buf_bytes(kGmTT);
+constexpr int kGmLdsBytes = kGmDummyOff + 1024;
 
 // Everything one pass over up to 16*NTT routed rows of one expert needs.
 struct GemmCtx {
@@ -63,28 +80,64 @@ struct GemmCtx {
 // One pass with NTT live token tiles (compile-time, so the MFMA loop is straight-line code and
 // LDS reads can be scheduled ahead of the MFMAs that use them).
 template <int ACT, int NTT>
-__device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint16_t* __restrict__ xs) {
+__device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict__ xs) {
   constexpr bool swiglu = (ACT == MOE_ACT_SWIGLU_OAI);
+  constexpr int BUF = gemm_buf_bytes(NTT);
+  // DMA instructions per wavefront per chunk: the chunk's NTT*4 KB split over the wavefronts,
+  // every wavefront issuing the same count (surplus ones copy zeros into a dummy KB) so that
+  // the vector-memory counter waits below are exact for each of them
+  constexpr int NX = (NTT * 4 + kGmWaves - 1) / kGmWaves;
+  constexpr int LOADS = NX + 2 * kGmWT;   // vector-memory instructions per wavefront per chunk
+  static_assert(2 * kGmWT + 2 * LOADS <= 63, "vmcnt range");
   const int C = g.C;
   const int lr = g.lr, lg = g.lg;
+  const int lane = g.tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(g.tid >> 6);   // uniform: LDS-DMA base
 
-  // weight fetch of chunk c into a ring slot (zeros past K); c is uniform
+  // weight fetch of chunk c into a ring slot. Chunks past K re-read the last chunk (their
+  // compute is skipped), so every chunk issues the same loads and only the last one differs
+  // (its narrower row pitch): one uniform select per offset, no branches.
   auto load_w = [&](int c, u32x4_t (&dq)[kGmWT], uint32_t (&dx)[kGmWT]) {
-    if (c < C) {
-      const uint32_t cq = (uint32_t)c * g.N * (kChunkBlocks * 16);
-      const uint32_t cs = (uint32_t)c * kChunkBlocks;   // scale byte of block 4c + lg
-      const bool last = (c == C - 1);
+    const int cc = min(c, C - 1);
+    const bool last = cc == C - 1;
+    const uint32_t cq = (uint32_t)cc * g.N * (kChunkBlocks * 16);
+    const uint32_t cs = (uint32_t)cc * kChunkBlocks;   // scale byte of block 4c + lg
 #pragma unroll
-      for (int t = 0; t < kGmWT; ++t) {
-        dq[t] = buf_load16(g.rq, last ? g.wol[t] : g.wo[t], cq);
-        dx[t] = buf_load8(g.rs, g.so[t], cs);
-      }
-    } else {
+    for (int t = 0; t < kGmWT; ++t) {
+      dq[t] = buf_load16(g.rq, last ? g.wol[t] : g.wo[t], cq);
+      dx[t] = buf_load8(g.rs, g.so[t], cs);
+    }
+  };
+
+  // activation DMA: instruction i of this wavefront covers 16-byte slots p = j*64 + lane,
+  // j = wave + 4*i, i.e. routed row m = p / 16 of the pass and swizzled slot p % 16, which holds
+  // the row's 16-byte piece q = (p % 16) ^ (m % 16) of the chunk
+  uint32_t xo[NX], xol[NX];
 #pragma unroll
-      for (int t = 0; t < kGmWT; ++t) {
-        dq[t] = u32x4_t{0u, 0u, 0u, 0u};
-        dx[t] = 127u;
-      }
+  for (int i = 0; i < NX; ++i) {
+    const int p = (wave + kGmWaves * i) * 64 + lane;
+    const int m = p >> 4, q = (p & 15) ^ (m & 15);
+    uint32_t off = kOOB;
+    if (m < g.live && wave + kGmWaves * i < NTT * 4) {
+      const int r = g.row0 + g.p0 + m;
+      const uint32_t src = g.a_row ? (uint32_t)g.a_row[r] : (uint32_t)r;
+      off = src * (uint32_t)g.K * 2 + q * 16;
+    }
+    xo[i] = off;
+    xol[i] = (q * 8 < g.klast) ? off : kOOB;   // the last chunk may be narrower than 128 k
+  }
+  auto load_x = [&](int c) {
+    const int cc = min(c, C - 1);
+    const bool last = cc == C - 1;
+    const int dst = (c % kGmXRing) * BUF;
+    const uint32_t ck = (uint32_t)cc * kGmRowBytes;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int j = wave + kGmWaves * i;   // uniform
+      const int d = j < NTT * 4 ? dst + j * 1024 : kGmDummyOff;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          g.ra, (__attribute__((address_space(3))) void*)(xs + d), 16, last ? xol[i] : xo[i], ck,
+          0, 0);
     }
   };
 
@@ -101,86 +154,64 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint16_t* __restrict
     for (int tt = 0; tt < NTT; ++tt) acc[t][tt] = f32x4_t{b[0], b[1], b[2], b[3]};
   }
 
-  // activation staging: thread -> (row = tid/16 + 16*pass, 16-byte piece = tid%16)
-  const int srow = g.tid >> 4, spiece = g.tid & 15;
-  const bool piece_in_last = spiece * 8 < g.klast;
-  uint32_t ao[NTT];
+  u32x4_t wq[kGmWRing][kGmWT];
+  uint32_t wx[kGmWRing][kGmWT];
+
+  __syncthreads();  // the previous pass is done with the LDS buffers
+  // prologue, in the steady state's issue order: W0 X0 W1 X1 W2 X2 W3
 #pragma unroll
-  for (int ps = 0; ps < NTT; ++ps) {
-    const int m = ps * 16 + srow;
-    uint32_t off = kOOB;
-    if (m < g.live) {
-      const int r = g.row0 + g.p0 + m;
-      const uint32_t src = g.a_row ? (uint32_t)g.a_row[r] : (uint32_t)r;
-      off = src * (uint32_t)g.K * 2 + spiece * 16;
+  for (int c = 0; c < kGmWRing; ++c) {
+    load_w(c, wq[c], wx[c]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c < kGmXRing - 1) {
+      load_x(c);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    ao[ps] = off;
   }
-  uint4 stage[NTT];
-  auto load_stage = [&](int c) {
-    const uint32_t ck = (uint32_t)c * kGmChunkK * 2;
-    const bool last = (c == C - 1);
-#pragma unroll
-    for (int ps = 0; ps < NTT; ++ps) {
-      const u32x4_t v = buf_load16(g.ra, (last && !piece_in_last) ? kOOB : ao[ps], ck);
-      stage[ps] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int ps = 0; ps < NTT; ++ps)
-      *reinterpret_cast<uint4*>(xs + buf * kGmBufElems + (ps * 16 + srow) * kGmPitch +
-                                spiece * 8) = stage[ps];
-  };
 
-  u32x4_t wq[kGmPF][kGmWT];
-  uint32_t wx[kGmPF][kGmWT];
-
-  load_stage(0);
-  __syncthreads();  // previous pass is done with both LDS buffers
-  store_stage(0);
-  if (C > 1) load_stage(1);
+  for (int c0 = 0; c0 < C; c0 += kGmWRing) {
 #pragma unroll
-  for (int pf = 0; pf < kGmPF; ++pf) load_w(pf, wq[pf], wx[pf]);
-
-  for (int c0 = 0; c0 < C; c0 += kGmPF) {
-#pragma unroll
-    for (int pf = 0; pf < kGmPF; ++pf) {
-      const int c = c0 + pf;
+    for (int sl = 0; sl < kGmWRing; ++sl) {
+      const int c = c0 + sl;
+      // issued after X(c): W(c+1), then two iterations' X and W -> waiting until only those
+      // are outstanding completes X(c) and W(c) (issued before it)
+      // A bare s_barrier, not __syncthreads(): its fence would also wait for the DMA copies of
+      // the chunks still in flight. Here the wait above has landed this wavefront's share of
+      // X(c) in LDS, and every wavefront consumed its LDS reads of chunk c - 1 (in its MFMAs)
+      // before arriving, so after the barrier X(c) is complete and buffer (c - 1) % 4 is free.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kGmWT + 2 * LOADS));
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      load_x(c + kGmXRing - 1);
+      __builtin_amdgcn_sched_barrier(0);
       if (c < C) {
-        __syncthreads();  // chunk c is in LDS; buffer (c+1)&1 is free
-        u32x4_t cq[kGmWT];
+        const uint8_t* xb = xs + (c % kGmXRing) * BUF;
         float cs[kGmWT];
 #pragma unroll
-        for (int t = 0; t < kGmWT; ++t) {
-          cq[t] = wq[pf][t];
-          cs[t] = e8m0_scale_operand(wx[pf][t]);
-        }
-        load_w(c + kGmPF, wq[pf], wx[pf]);   // refill this ring slot (zeros past K)
-        const uint16_t* xb = xs + (pf & 1) * kGmBufElems;   // c0 is even: c & 1 == pf & 1
+        for (int t = 0; t < kGmWT; ++t) cs[t] = e8m0_scale_operand(wx[sl][t]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           bf16x8_t A[kGmWT];
 #pragma unroll
-          for (int t = 0; t < kGmWT; ++t) A[t] = dequant8(cq[t][i], cs[t]);
-          bf16x8_t B[NTT];
+          for (int t = 0; t < kGmWT; ++t) A[t] = dequant8(wq[sl][t][i], cs[t]);
 #pragma unroll
-          for (int tt = 0; tt < NTT; ++tt)
-            B[tt] = *reinterpret_cast<const bf16x8_t*>(xb + (tt * 16 + lr) * kGmPitch + lg * 32 +
-                                                       i * 8);
-#pragma unroll
-          for (int tt = 0; tt < NTT; ++tt)
+          for (int tt = 0; tt < NTT; ++tt) {
+            const int m = tt * 16 + lr;   // m % 16 == lr
+            const bf16x8_t B =
+                *reinterpret_cast<const bf16x8_t*>(xb + (m * 16 + ((lg * 4 + i) ^ lr)) * 16);
 #pragma unroll
             for (int t = 0; t < kGmWT; ++t)
-              acc[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t], B[tt], acc[t][tt], 0, 0, 0);
-        }
-        if (c + 1 < C) {
-          store_stage((pf + 1) & 1);
-          if (c + 2 < C) load_stage(c + 2);
+              acc[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t], B, acc[t][tt], 0, 0, 0);
+          }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(c + kGmWRing, wq[sl], wx[sl]);   // refill the slot chunk c used, in place
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no LDS-DMA write outlives the pass
 
   // epilogue: lane holds rows 4*lg..4*lg+3 of each weight tile for token column lr
 #pragma unroll
@@ -190,13 +221,13 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint16_t* __restrict
     const size_t r = (size_t)(g.row0 + g.p0 + m);
     if (swiglu) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 1; ++t) {
         const int j0 = g.tile_base[t] + 4 * lg;
         uint16_t h[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           h[i] = (uint16_t)f32_to_bf16_bits(
-              swiglu_oai(acc[t][tt][i], acc[t + 2][tt][i], g.alpha, g.limit));
+              swiglu_oai(acc[t][tt][i], acc[t + 1][tt][i], g.alpha, g.limit));
         uint16_t* dst = reinterpret_cast<uint16_t*>(g.out) + r * g.F + j0;
         if (4 * lg + 4 <= g.rows_in[t] && (g.F & 3) == 0) {
           *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
@@ -228,10 +259,10 @@ gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
             const float* __restrict__ bias, const int32_t* __restrict__ counts,
             const int32_t* __restrict__ basep, int E, int N, int K, float alpha, float limit,
             void* __restrict__ out) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
-  __shared__ int scratch[2];
-  const int e = slot_expert(counts, E, (int)blockIdx.y, scratch);
-  if (e < 0) return;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  const int c64 = ((int)(threadIdx.x & 63) < E) ? counts[threadIdx.x & 63] : 0;
+  const int e = wave_slot_expert(counts, E, (int)blockIdx.y, c64);
+  if (e < 0) return;   // uniform over the workgroup: fewer live experts than slots
   constexpr bool swiglu = (ACT == MOE_ACT_SWIGLU_OAI);
   GemmCtx g;
   g.a_row = a_row;
@@ -258,11 +289,11 @@ gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
 #pragma unroll
   for (int t = 0; t < kGmWT; ++t) {
     if (swiglu) {
-      const int jb = (int)blockIdx.x * 128 + wave * 32 + (t & 1) * 16;
-      g.tile_base[t] = (t < 2) ? jb : g.F + jb;
+      const int jb = (int)blockIdx.x * 128 + wave * 16;   // tile 0: gate rows, tile 1: up rows
+      g.tile_base[t] = (t == 0) ? jb : g.F + jb;
       g.rows_in[t] = min(16, g.F - jb);
     } else {
-      g.tile_base[t] = (int)blockIdx.x * 256 + wave * 64 + t * 16;
+      g.tile_base[t] = (int)blockIdx.x * 256 + wave * 32 + t * 16;
       g.rows_in[t] = min(16, N - g.tile_base[t]);
     }
   }
