@@ -50,12 +50,18 @@ namespace moe {
 
 constexpr int kGmWaves = 8;              // 2 wavefronts per SIMD
 constexpr int kGmThreads = 64 * kGmWaves;
-constexpr int kGmWT = 2;                 // weight tiles (16 rows each) per wavefront
+constexpr int kGmMaxWT = 3;              // weight tiles (16 rows each) per wavefront, at most
+// SwiGLU: 2 tiles (16 gate rows + the matching 16 up rows); plain: 3 tiles (384 rows per
+// workgroup), which at gpt-oss shapes makes the down projection's grid a whole number of
+// rounds over the 256 CUs (2880 / 384 -> 8 workgroups per expert)
+__host__ __device__ constexpr int gemm_wt(int act) { return act == MOE_ACT_SWIGLU_OAI ? 2 : 3; }
 constexpr int kGmTT = 8;                 // token tiles (16 rows each) per pass: 128 routed rows
 constexpr int kGmChunkK = 128;           // k per chunk = 4 MX blocks
 constexpr int kGmRowBytes = kGmChunkK * 2;   // activation bytes per row per chunk
 
-constexpr int kGmWRing = 4;              // weight chunks in flight (register ring slots)
+// weight chunks in flight (register ring slots): 4 with 2 tiles per wavefront, 3 with 3 tiles
+// (registers); the activation chunks are issued 3 ahead either way
+__host__ __device__ constexpr int gemm_wring(int wt) { return wt == 2 ? 4 : 3; }
 constexpr int kGmXRing = 4;              // activation chunk buffers in LDS (3 chunks ahead)
 // LDS of a pass with NTT token tiles
 __host__ __device__ constexpr int gemm_buf_bytes(int ntt) { return ntt * 16 * kGmRowBytes; }
@@ -72,9 +78,9 @@ struct GemmCtx {
   int e, N, K, C, klast, row0, p0, live, F;
   int tid, lr, lg;
   float alpha, limit;
-  int tile_base[kGmWT];
-  int rows_in[kGmWT];
-  uint32_t wo[kGmWT], wol[kGmWT], so[kGmWT];
+  int tile_base[kGmMaxWT];
+  int rows_in[kGmMaxWT];
+  uint32_t wo[kGmMaxWT], wol[kGmMaxWT], so[kGmMaxWT];
 };
 
 // One pass with NTT live token tiles (compile-time, so the MFMA loop is straight-line code and
@@ -82,6 +88,7 @@ struct GemmCtx {
 template <int ACT, int NTT>
 __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict__ xs) {
   constexpr bool swiglu = (ACT == MOE_ACT_SWIGLU_OAI);
+  constexpr int kGmWT = gemm_wt(ACT);
   constexpr int BUF = gemm_buf_bytes(NTT);
   // DMA instructions per wavefront per chunk: the chunk's NTT*4 KB split over the wavefronts,
   // every wavefront issuing the same count (surplus ones copy zeros into a dummy KB) so that
@@ -154,17 +161,25 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
     for (int tt = 0; tt < NTT; ++tt) acc[t][tt] = f32x4_t{b[0], b[1], b[2], b[3]};
   }
 
+  constexpr int kGmWRing = gemm_wring(kGmWT);
   u32x4_t wq[kGmWRing][kGmWT];
   uint32_t wx[kGmWRing][kGmWT];
 
   __syncthreads();  // the previous pass is done with the LDS buffers
-  // prologue, in the steady state's issue order: W0 X0 W1 X1 W2 X2 W3
+  // prologue, in the steady state's issue order (W0 X0 W1 X1 W2 X2 W3 with a ring of 4;
+  // X0 W0 X1 W1 X2 W2 with a ring of 3)
 #pragma unroll
-  for (int c = 0; c < kGmWRing; ++c) {
-    load_w(c, wq[c], wx[c]);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int c = 0; c < 4; ++c) {
+    if (kGmWRing == 4 && c < kGmWRing) {
+      load_w(c, wq[c], wx[c]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (c < kGmXRing - 1) {
       load_x(c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kGmWRing == 3 && c < kGmWRing) {
+      load_w(c, wq[c], wx[c]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -173,8 +188,9 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
 #pragma unroll
     for (int sl = 0; sl < kGmWRing; ++sl) {
       const int c = c0 + sl;
-      // issued after X(c): W(c+1), then two iterations' X and W -> waiting until only those
-      // are outstanding completes X(c) and W(c) (issued before it)
+      // issued after X(c): one weight chunk, then two iterations' X and W -> waiting until only
+      // those are outstanding completes X(c) (and W(c) with the ring of 4, issued before it;
+      // with the ring of 3 the register dependency makes the compiler wait for W(c))
       // A bare s_barrier, not __syncthreads(): its fence would also wait for the DMA copies of
       // the chunks still in flight. Here the wait above has landed this wavefront's share of
       // X(c) in LDS, and every wavefront consumed its LDS reads of chunk c - 1 (in its MFMAs)
@@ -285,7 +301,8 @@ gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
   g.row0 = basep[e];
   const int cnt = counts[e];
 
-  // weight rows of the wavefront's 4 tiles (first row, rows that exist)
+  // weight rows of the wavefront's tiles (first row, rows that exist)
+  constexpr int kGmWT = gemm_wt(ACT);
 #pragma unroll
   for (int t = 0; t < kGmWT; ++t) {
     if (swiglu) {
@@ -293,7 +310,7 @@ gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
       g.tile_base[t] = (t == 0) ? jb : g.F + jb;
       g.rows_in[t] = min(16, g.F - jb);
     } else {
-      g.tile_base[t] = (int)blockIdx.x * 256 + wave * 32 + t * 16;
+      g.tile_base[t] = (int)blockIdx.x * (kGmWaves * kGmWT * 16) + (wave * kGmWT + t) * 16;
       g.rows_in[t] = min(16, N - g.tile_base[t]);
     }
   }
@@ -339,7 +356,9 @@ int moe_launch_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, con
   // buffer resources address at most 2 GB: one expert's weights and the activation matrix
   if ((int64_t)w->N * w->K / 2 >= (1LL << 31) || a_rows * w->K * 2 >= (1LL << 31))
     return MOE_ESHAPE;
-  const int64_t bx = (act == MOE_ACT_SWIGLU_OAI) ? (w->N / 2 + 127) / 128 : (w->N + 255) / 256;
+  const int64_t rows_per_wg = 16 * moe::kGmWaves * moe::gemm_wt(MOE_ACT_NONE);
+  const int64_t bx = (act == MOE_ACT_SWIGLU_OAI) ? (w->N / 2 + 127) / 128
+                                                 : (w->N + rows_per_wg - 1) / rows_per_wg;
   int64_t slots = mpad_max / tile_m;
   if (slots > w->E) slots = w->E;
   static bool lds_attr_set = false;  // > 64 KB of dynamic LDS must be opted into once
