@@ -40,6 +40,9 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=12.0)
+    p.add_argument("--counter-pass", action="store_true",
+                   help="run only what the hardware-counter passes measure: a plain copy kernel of "
+                        "known size, then the fused decode of 8 layers twice (no timing, no JSON)")
     return p.parse_args()
 
 
@@ -203,6 +206,53 @@ def cpu_baseline(synth, wl, budget_s):
                       f"scaled to 24 layers"}
 
 
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "decode_gate_up_kernel_traffic_decode_t1.md")
+TRAFFIC_SOURCES = ("decode.hip", "gemv_core.hpp", "route_core.hpp", "common.hpp")
+
+
+def kernel_source_hash():
+    """sha256 over the sources of the fused decode kernels (any change invalidates counters)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "mxfp4_mixture_experts_route_amd", "csrc")
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused gate_up kernel from the committed counter summary, or
+    None when there is none or the kernel's sources changed since the counters were taken."""
+    try:
+        fields = dict(line.strip("` \n").split("=", 1) for line in open(TRAFFIC_FILE)
+                      if line.startswith("`") and "=" in line)
+    except OSError:
+        return None
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    return int(float(fields["traffic_bytes_per_launch"]))
+
+
+def counter_pass(moe, synth, torch):
+    """Workload of the rocprofv3 --pmc passes: a copy kernel of 64 MiB (read 64 MiB, write
+    64 MiB) three times for the counters' scale, then mx4_moe_decode over 8 layers, twice."""
+    src = torch.ones(16 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    wl = synth.WORKLOADS["decode_t1"]
+    layers = build_layers(moe, synth, torch, wl, "gemv", 8)
+    for _ in range(2):
+        for L in layers:
+            L.decode()
+    torch.cuda.synchronize()
+    log("counter pass done")
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -215,6 +265,9 @@ def main():
     from mxfp4_mixture_experts_route_amd import synth
     moe.lib()   # fail loudly if the HIP library is missing
     torch.cuda.init()
+    if args.counter_pass:
+        counter_pass(moe, synth, torch)
+        return
     sleep_cycles = sleep_cycles_for(torch, 20.0)
 
     # ---------------- headline: decode, T=1, 24 MoE layers ----------------
@@ -262,7 +315,8 @@ def main():
                    "chain": "mx4_moe_decode (2 launches per layer)", "graph": "hip graph replay"},
         "roofline": {"kernel": "decode_gate_up_kernel (routing + gate_up + SwiGLU-OAI)",
                      "bound": "hbm", "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(),
                      "bytes_per_launch": int(gu_bytes), "avg_launch_us": round(fused_us[0], 3)},
         "decode": {"fused": {"gate_up_kernel_us": round(fused_us[0], 3),
                              "down_combine_kernel_us": round(fused_us[1], 3),
