@@ -290,16 +290,18 @@ extern "C" int mx4_moe_decode(const float* logits, const uint16_t* x, int64_t T,
   const int C2 = (F / 32 + moe::kChunkBlocks - 1) / moe::kChunkBlocks;
   const int R = (int)T * k;
 
-  // launch 1: workgroups of up to 4 wavefronts (ksplit * units), grid (units, R + 1)
-  const int ks1 = C1 > moe::kGvSegSplit ? 2 : 1;
+  // launch 1: workgroups of ksplit * (1, 2 or 4 row groups) wavefronts, grid (units, R + 1)
+  const int ks1 = moe::gv_ksplit(C1);
   const int units1 = (F + 7) / 8;
   const int64_t waves_total = (int64_t)units1 * R * ks1;
-  int waves1 = 4;
-  while (waves1 > ks1 && waves_total / waves1 < 640) waves1 >>= 1;
+  int upw1 = 256 / 64 / ks1;
+  while (upw1 > 1 && waves_total / (upw1 * ks1) < 640) upw1 >>= 1;
+  const int waves1 = upw1 * ks1;
   const size_t lds1 = (((size_t)D * 2 + 1023) & ~(size_t)1023) + 64 +
                       (ks1 > 1 ? (size_t)waves1 * 64 * 16 : 0);
-  // launch 2: one workgroup per (16 rows, token), a wavefront (or K-split pair) per slot
-  const int ks2 = (C2 > moe::kGvSegSplit && 2 * k * 64 <= moe::kDecMaxThreads) ? 2 : 1;
+  // launch 2: one workgroup per (16 rows, token), ksplit wavefronts per slot
+  int ks2 = moe::gv_ksplit(C2);
+  while (ks2 > 1 && k * ks2 * 64 > moe::kDecMaxThreads) --ks2;
   const int waves2 = k * ks2;
   const size_t lds2 = (((size_t)k * F * 2 + 1023) & ~(size_t)1023) + 64 + (size_t)waves2 * 64 * 16;
   if (lds1 > 65536 || lds2 > 65536 || 64 * waves2 > moe::kDecMaxThreads) return MOE_ESHAPE;
@@ -309,22 +311,13 @@ extern "C" int mx4_moe_decode(const float* logits, const uint16_t* x, int64_t T,
     return MOE_ESHAPE;
 
   hipStream_t st = (hipStream_t)stream;
-  const dim3 g1((unsigned)((units1 + waves1 / ks1 - 1) / (waves1 / ks1)), (unsigned)(R + 1));
-  if (ks1 > 1)
-    moe::launch(moe::decode_gate_up_kernel<moe::kGvSegSplit>, g1, dim3(64 * waves1), lds1, st,
-                       logits, x, (int)T, E, k, w_gu->q, w_gu->s, w_gu->bias, N, D, alpha, limit,
-                       ks1, ids, w, counts, basep, row_tok, pos, h);
-  else
-    moe::launch(moe::decode_gate_up_kernel<moe::kGvSeg>, g1, dim3(64 * waves1), lds1, st,
-                       logits, x, (int)T, E, k, w_gu->q, w_gu->s, w_gu->bias, N, D, alpha, limit,
-                       ks1, ids, w, counts, basep, row_tok, pos, h);
+  const dim3 g1((unsigned)((units1 + upw1 - 1) / upw1), (unsigned)(R + 1));
+  moe::launch(moe::decode_gate_up_kernel<moe::kGvSeg>, g1, dim3(64 * waves1), lds1, st, logits, x,
+              (int)T, E, k, w_gu->q, w_gu->s, w_gu->bias, N, D, alpha, limit, ks1, ids, w, counts,
+              basep, row_tok, pos, h);
   if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
   const dim3 g2((unsigned)((D + 15) / 16), (unsigned)T);
-  if (ks2 > 1)
-    moe::launch(moe::decode_down_kernel<moe::kGvSegSplit>, g2, dim3(64 * waves2), lds2, st, h,
-                       k, ids, w, w_dn->q, w_dn->s, w_dn->bias, D, F, ks2, d, y);
-  else
-    moe::launch(moe::decode_down_kernel<moe::kGvSeg>, g2, dim3(64 * waves2), lds2, st, h, k,
-                       ids, w, w_dn->q, w_dn->s, w_dn->bias, D, F, ks2, d, y);
+  moe::launch(moe::decode_down_kernel<moe::kGvSeg>, g2, dim3(64 * waves2), lds2, st, h, k, ids, w,
+              w_dn->q, w_dn->s, w_dn->bias, D, F, ks2, d, y);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

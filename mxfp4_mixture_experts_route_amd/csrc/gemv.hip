@@ -205,41 +205,30 @@ int moe_launch_gemv(const uint16_t* a, const int32_t* a_row, int64_t a_rows, con
   const int units = (act == MOE_ACT_SWIGLU_OAI) ? (w->N / 2 + 7) / 8 : (w->N + 15) / 16;
   int64_t slots = mpad_max / tile_m;
   if (slots > w->E) slots = w->E;
-  // K over two wavefronts when it takes more than one short segment: twice the wavefronts,
-  // each with half the loads in flight, keep the decode closer behind the weight stream
-  const int ksplit = C > moe::kGvSegSplit ? 2 : 1;
-  // Wavefronts per workgroup: as many as keep >= ~2.5 workgroups per CU (256 CUs), so that the
-  // uneven last round of workgroups costs little; more wavefronts share one activation staging.
+  // K over up to 4 wavefronts (12 chunks each): shorter wavefronts keep the decode close behind
+  // the weight stream. Row groups per workgroup: as many as keep >= ~2.5 workgroups per CU (256
+  // CUs); more wavefronts share one activation staging.
+  const int ksplit = moe::gv_ksplit(C);
   const int64_t total_waves = (int64_t)units * slots * ksplit;
-  int waves = 4;
-  while (waves > ksplit && total_waves / waves < 640) waves >>= 1;
+  int upw = moe::kGvMaxThreads / 64 / ksplit;   // row groups per workgroup
+  while (upw > 1 && total_waves / (upw * ksplit) < 640) upw >>= 1;
+  const int waves = upw * ksplit;
   const int threads = 64 * waves;
   const size_t all_bytes = ((size_t)a_rows * row_bytes + 1023) & ~(size_t)1023;
   const int stage_all = all_bytes <= (size_t)moe::kGvStageAll ? 1 : 0;
-  int rb = (int)((moe::kGvLdsBudget - 64) / row_bytes);   // rows + the zero block
+  int rb = (int)((moe::kGvLdsBudget - 64 - (size_t)threads * 16) / row_bytes);
   if (rb > moe::kGvCols) rb = moe::kGvCols;
   if (rb < 1) return MOE_ESHAPE;
   const size_t lds = (stage_all ? all_bytes : (size_t)rb * row_bytes) + 64 +
                      (ksplit > 1 ? (size_t)threads * 16 : 0);
-  const int64_t bx = (units + waves / ksplit - 1) / (waves / ksplit);
+  const int64_t bx = (units + upw - 1) / upw;
   const dim3 grid((unsigned)bx, (unsigned)slots), block((unsigned)threads);
-  if (act == MOE_ACT_SWIGLU_OAI) {
-    if (ksplit > 1)
-      launch_gemv<MOE_ACT_SWIGLU_OAI, moe::kGvSegSplit>(grid, block, lds, stream, a, a_row, a_rows, w,
-                                                         counts, basep, alpha, limit, out, rb,
-                                                         stage_all, ksplit);
-    else
-      launch_gemv<MOE_ACT_SWIGLU_OAI, moe::kGvSeg>(grid, block, lds, stream, a, a_row, a_rows, w,
-                                                    counts, basep, alpha, limit, out, rb,
-                                                    stage_all, ksplit);
-  } else {
-    if (ksplit > 1)
-      launch_gemv<MOE_ACT_NONE, moe::kGvSegSplit>(grid, block, lds, stream, a, a_row, a_rows, w,
-                                                   counts, basep, alpha, limit, out, rb, stage_all,
-                                                   ksplit);
-    else
-      launch_gemv<MOE_ACT_NONE, moe::kGvSeg>(grid, block, lds, stream, a, a_row, a_rows, w, counts,
-                                              basep, alpha, limit, out, rb, stage_all, ksplit);
-  }
+  if (act == MOE_ACT_SWIGLU_OAI)
+    launch_gemv<MOE_ACT_SWIGLU_OAI, moe::kGvSeg>(grid, block, lds, stream, a, a_row, a_rows, w,
+                                                  counts, basep, alpha, limit, out, rb, stage_all,
+                                                  ksplit);
+  else
+    launch_gemv<MOE_ACT_NONE, moe::kGvSeg>(grid, block, lds, stream, a, a_row, a_rows, w, counts,
+                                            basep, alpha, limit, out, rb, stage_all, ksplit);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

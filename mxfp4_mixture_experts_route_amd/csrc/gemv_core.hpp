@@ -13,7 +13,7 @@
 //  * Weights are in the chunked layout (chunks of 4 MX blocks, all rows of a chunk together).
 //    Lane (r = lane%16, g = lane/16) takes block g of every chunk of row r, so each load
 //    instruction of the wavefront reads one contiguous 1 KB run.
-//  * A segment of up to SEG chunks is loaded at once, in K order: for every 4 chunks their scale
+//  * A segment of SEG = 12 chunks is loaded at once, in K order: for every 4 chunks their scale
 //    dword group (one dwordx4: a lane's scale for chunk c is byte g of dword c of its 16-byte
 //    padded scale row), then their nibbles. Loads complete in issue order, so chunk i is computed
 //    as soon as its own bytes arrive. All loads are buffer loads with offsets computed once;
@@ -31,8 +31,16 @@
 
 namespace moe {
 
-constexpr int kGvSeg = 24;        // chunks per K segment, all in flight at once (K <= 3072: one)
-constexpr int kGvSegSplit = 12;   // the same when K is split over two wavefronts
+constexpr int kGvSeg = 12;        // chunks per K segment and wavefront, all in flight at once
+constexpr int kGvMaxSplit = 4;    // K is split over up to this many wavefronts of the same rows
+
+// Wavefronts that share one set of 16 rows: one per 12 chunks of K, at most 4 (longer K runs
+// several segments per wavefront). (Measured at gpt-oss K = 23 chunks: 2 wavefronts of 12 beat
+// 3 of 8, whose smaller workgroups stage the activations twice as often.)
+__host__ __device__ constexpr int gv_ksplit(int C) {
+  return C <= kGvSeg ? 1 : (C + kGvSeg - 1) / kGvSeg > kGvMaxSplit ? kGvMaxSplit
+                                                                   : (C + kGvSeg - 1) / kGvSeg;
+}
 constexpr int kGvPF = 1;          // B fragments read this many chunks ahead
 
 // Expert of a slot: the slot-th expert with a non-zero count, or -1. c64 is this lane's
@@ -159,7 +167,7 @@ struct Mx4Wave {
 };
 
 // Chunk range [cb, ce) of K part `part` of `ksplit`: parts take Cp chunks each, Cp a multiple of
-// 4 (whole scale dword groups).
+// 4 (whole scale dword groups). gpt-oss K = 2880 is 23 chunks: parts of 12 and 11.
 __device__ __forceinline__ void k_part_range(int C, int part, int ksplit, int& cb, int& ce,
                                              int& Cp) {
   Cp = ((C + ksplit - 1) / ksplit + 3) & ~3;
