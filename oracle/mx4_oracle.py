@@ -120,6 +120,71 @@ def bf16_round(x) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------------------------
+# MXFP8 activations (the variant of the projections on the MX-scaled MFMA). The pages quantize
+# only the weights; every fact of this section is [ext]: the OCP 8-bit floating point spec
+# (E4M3) and the OCP MX v1.0 spec (its conversion of a 32-value block to a shared e8m0 scale
+# plus elements).
+# --------------------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0   # largest finite E4M3 magnitude: exponent field 15, mantissa 110
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each FP8 E4M3 byte [ext]: bit 7 = sign, bits 6..3 = exponent (bias 7), bits
+    2..0 = mantissa; exponent field 0 holds the subnormals m * 2^-9; the two bytes with all of
+    bits 6..0 set are NaN; there are no infinities."""
+    c = np.asarray(codes, dtype=np.int64)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, (e - 7).astype(np.int32)))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+# magnitude -> code of the 127 finite non-negative E4M3 values
+_E4M3_CODE_OF = {float(v): c for c, v in enumerate(e4m3_decode(np.arange(127)))}
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 code of each finite float64 value, ties to the even mantissa, magnitudes
+    beyond the largest finite value saturating to it (the MX conversion clamps instead of
+    producing NaN) [ext]. Written from the format: values near |v| are spaced 2^(e-4) apart
+    for frexp exponent e, floored at the subnormal spacing 2^-9. The sign bit is the value's,
+    so -0.0 and negatives that round to zero give 0x80."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    quantum = np.ldexp(1.0, np.maximum(e, -5) - 4)
+    r = np.minimum(np.rint(a / quantum) * quantum, E4M3_MAX)       # rint: half to even
+    mag = np.array([_E4M3_CODE_OF[float(x)] for x in r.ravel()], dtype=np.int64).reshape(r.shape)
+    return (mag | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def mx8_quantize(a_bits):
+    """MXFP8 (E4M3 elements) of bf16 rows [rows][K] -> (codes u8 [rows][K], scales u8
+    [rows][K/32]) by the OCP MX v1.0 conversion [ext]: for each block of 32 consecutive values,
+    the shared exponent is floor(log2(max |v|)) minus 8 (the exponent of E4M3's largest
+    normal), clamped to e8m0's range [-127, 127]; each element is e4m3_encode(v / 2^X), exact
+    division by a power of two. Reading (the spec leaves it free): an all-zero block takes the
+    smallest scale, X = -127 (the clamp of log2(0) = -inf). Inputs must be finite."""
+    a = bf16_to_f64(a_bits)
+    rows, K = a.shape
+    assert K % 32 == 0
+    blocks = a.reshape(rows, K // 32, 32)
+    amax = np.abs(blocks).max(axis=-1)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))                  # amax in [2^(e-1), 2^e)
+    X = np.where(amax > 0, np.clip(e - 1 - 8, -127, 127), -127)
+    codes = e4m3_encode(blocks / np.ldexp(1.0, X.astype(np.int32))[..., None])
+    return codes.reshape(rows, K), (X + 127).astype(np.uint8)
+
+
+def mx8_dequant(codes, scales) -> np.ndarray:
+    """Values of MXFP8 rows: e4m3(code) * 2^(s-127) for the element's 32-value block, float64
+    (exact)."""
+    return e4m3_decode(codes) * np.repeat(e8m0_decode(scales), 32, axis=-1)
+
+
+# --------------------------------------------------------------------------------------------
 # routing and bucketing
 # --------------------------------------------------------------------------------------------
 
@@ -218,9 +283,21 @@ def project(a_bits, a_row, q, s, bias, counts, basep, mpad: int):
     sum rounds, at float64). Also returns S[r][n] = |bias| + sum_i |x_r[i] * W[e][n][i]|, the
     scale of the fp32 summation error bound. Rows that are not live are NaN in both.
     """
+    return project_values(bf16_to_f64(a_bits), a_row, q, s, bias, counts, basep, mpad)
+
+
+def project_mx8(a_codes, a_scales, a_row, q, s, bias, counts, basep, mpad: int):
+    """The projection of `project` with MXFP8 activation rows (codes [rows][K], scales
+    [rows][K/32], as mx8_quantize returns them) in place of bf16 rows: x_r is the exact value of
+    the quantized row, and everything else is unchanged."""
+    return project_values(mx8_dequant(a_codes, a_scales), a_row, q, s, bias, counts, basep,
+                          mpad)
+
+
+def project_values(a, a_row, q, s, bias, counts, basep, mpad: int):
+    """The projection of `project` with the activation rows given as float64 values [rows][K]."""
     E, N, _ = q.shape
     K = q.shape[2] * 2
-    a = bf16_to_f64(a_bits)
     out = np.full((mpad, N), np.nan, dtype=np.float64)
     S = np.full((mpad, N), np.nan, dtype=np.float64)
     for e in range(E):
@@ -242,16 +319,27 @@ def project(a_bits, a_row, q, s, bias, counts, basep, mpad: int):
 def project_at(a_bits, a_row, q, s, bias, counts, basep, samples):
     """The same projection as `project`, evaluated only at the sampled (row, n) pairs (rows must
     be live). For full-size checks where the whole product is too slow on the CPU."""
+    a = np.asarray(a_bits)
+    return _project_at(lambda src: bf16_to_f64(a[src]), a_row, q, s, bias, counts, basep,
+                       samples)
+
+
+def project_mx8_at(a_codes, a_scales, a_row, q, s, bias, counts, basep, samples):
+    """project_mx8 evaluated only at the sampled (row, n) pairs (rows must be live)."""
+    return _project_at(lambda src: mx8_dequant(a_codes[src], a_scales[src]), a_row, q, s, bias,
+                       counts, basep, samples)
+
+
+def _project_at(row_values, a_row, q, s, bias, counts, basep, samples):
     basep = np.asarray(basep)
     counts = np.asarray(counts)
-    a = np.asarray(a_bits)
     vals = np.empty(len(samples), dtype=np.float64)
     S = np.empty(len(samples), dtype=np.float64)
     for i, (r, n) in enumerate(samples):
         e = int(np.searchsorted(basep, r, side="right") - 1)
         assert basep[e] <= r < basep[e] + counts[e], "sampled row is not live"
         src = r if a_row is None else int(a_row[r])
-        x = bf16_to_f64(a[src])
+        x = row_values(src)
         w = dequant(q[e, n][None, :], s[e, n][None, :])[0].astype(np.float64)
         b = 0.0 if bias is None else float(bias[e, n])
         with np.errstate(invalid="ignore", over="ignore"):
@@ -318,3 +406,28 @@ def chain(x_bits, logits, gate_up, down, k: int, tile_m: int, alpha: float, limi
     return {"ids": ids, "w": w, "mpad": mpad, "counts": counts, "basep": basep,
             "row_tok": row_tok, "pos": pos, "g": g, "g_S": g_S, "h": h, "d": d, "d_S": d_S,
             "y": y, "y_S": y_S}
+
+
+def chain_mx8(x_bits, logits, gate_up, down, k: int, tile_m: int, alpha: float, limit: float):
+    """The layer of `chain` with both projections on MXFP8 activations: the token rows x are
+    quantized once (mx8_quantize) and gathered by the gate_up projection; the bf16 h rows are
+    quantized after the SwiGLU-OAI (rows that are not live hold zeros and are never read) and
+    feed the down projection. Routing, CSR, SwiGLU-OAI, the bf16 rounding of h and the combine
+    are those of `chain`."""
+    T = x_bits.shape[0]
+    E = gate_up["q"].shape[0]
+    ids, w = route_topk(logits, k)
+    mpad = mpad_max(T, k, E, tile_m)
+    counts, basep, row_tok, pos = bucket(ids, E, tile_m, mpad)
+    xq, xs = mx8_quantize(x_bits)
+    g, g_S = project_mx8(xq, xs, row_tok, gate_up["q"], gate_up["s"], gate_up["bias"],
+                         counts, basep, mpad)
+    live = [r for _, r in live_rows(counts, basep)]
+    h = np.zeros((mpad, g.shape[1] // 2), dtype=np.uint16)
+    h[live] = bf16_round(swiglu_oai(g[live], alpha, limit))
+    hq, hs = mx8_quantize(h)
+    d, d_S = project_mx8(hq, hs, None, down["q"], down["s"], down["bias"], counts, basep, mpad)
+    y, y_S = combine(d, pos, w)
+    return {"ids": ids, "w": w, "mpad": mpad, "counts": counts, "basep": basep,
+            "row_tok": row_tok, "pos": pos, "xq": xq, "xs": xs, "g": g, "g_S": g_S, "h": h,
+            "hq": hq, "hs": hs, "d": d, "d_S": d_S, "y": y, "y_S": y_S}
