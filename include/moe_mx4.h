@@ -10,6 +10,11 @@
  *   mx4_moe_gemm    the same function on MFMA, many rows per expert (prefill)
  *   moe_combine     router-weighted sum of each token's expert rows, in slot order
  *
+ * with MXFP8 activations on the MX-scaled MFMA (a variant; formats from the OCP specs):
+ *
+ *   mx8_quantize      bf16 rows -> MXFP8 rows (E4M3 + one e8m0 scale per 32 values)
+ *   mx4_moe_gemm_mx8  the projection of mx4_moe_gemm over MXFP8 activation rows
+ *
  * and, for decode (a few tokens), the same chain fused into two launches:
  *
  *   mx4_moe_decode  logits + x -> routing, CSR, h, (d), y
@@ -192,6 +197,52 @@ int mx4_moe_gemv(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const 
 int mx4_moe_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const mx4_experts* w,
                  const int32_t* counts, const int32_t* basep, int tile_m, int64_t mpad_max,
                  int act, float alpha, float limit, void* out, void* stream);
+
+/*
+ * MXFP8 activations: the projections on the MX-scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4,
+ * E2M1 weights x E4M3 activations, each 32-value block carrying its own e8m0 scale). The pages
+ * quantize only the weights: this variant and every fact of its format come from outside them,
+ * the OCP 8-bit floating point spec (E4M3) and the OCP Microscaling v1.0 spec (conversion of a
+ * 32-value block to one shared e8m0 scale plus 32 elements). It changes the numerics: the
+ * activations are rounded to 4 significant bits before the product.
+ *
+ * MXFP8 row layout: row r of K values has its K E4M3 bytes at q + r*K (element i = byte i) and
+ * its K/32 e8m0 bytes at s + r*SP, SP = roundup(K/32, 16); the SP - K/32 padding bytes are 0.
+ *
+ * mx8_quantize: the OCP MX conversion of bf16 rows, exactly (bit for bit) as follows. For each
+ * block of 32 consecutive values with largest magnitude m: the shared exponent is
+ * X = floor(log2(m)) - 8 (8 = exponent of E4M3's largest normal), clamped to [-127, 127];
+ * a block of zeros (or of magnitudes below 2^-126) takes X = -127; its scale byte is X + 127.
+ * Each element is v / 2^X rounded to the nearest E4M3 value, ties to the even mantissa,
+ * magnitudes beyond 448 saturating to 448 (never NaN); the sign bit is v's, so -0 and negatives
+ * that round to zero give byte 0x80.
+ *   a     bf16 [rows][K] row-major, finite values (not checked).
+ *   live  i32 [rows] or NULL: rows with live[r] < 0 are skipped (q and s rows left unwritten),
+ *         e.g. the row_tok array of moe_bucket when quantizing h, whose padding and ghost rows
+ *         hold nothing.
+ *   q     u8 [rows][K] out; s u8 [rows][SP] out (padding bytes written 0).
+ * Errors: MOE_EINVAL for NULL a/q/s or rows < 1; MOE_ESHAPE for K < 32, K % 32 != 0 or
+ *         rows * K >= 2^31; MOE_EALIGN for a, q or s not 16-byte aligned; MOE_ELAUNCH.
+ *
+ * mx4_moe_gemm_mx8: the function of mx4_moe_gemm with activation row x = the MXFP8 row
+ * a_row[r] (or r) of (aq, as) in place of a bf16 row: g[n] = bias[e][n] + sum_i x[i]*W[e][n][i]
+ * with x[i] = e4m3(aq[..][i]) * 2^(as[..][i/32] - 127), accumulated in fp32 by the MFMA
+ * (products are exact; the hardware's sum over a 128-value step is not rounded like a chain of
+ * fp32 additions but stays within the same error bound, |error| <= 1e-3 * sum |x_i W_i|).
+ * Arguments, row semantics, epilogue (MOE_ACT_NONE / MOE_ACT_SWIGLU_OAI) and outputs as
+ * mx4_moe_gemm; a_rows counts MXFP8 rows.
+ * Errors: as mx4_moe_gemm (aq in place of a, also NULL as), plus MOE_ESHAPE for
+ *         K > MOE_MX8_GEMM_MAX_K and MOE_EALIGN for as not 16-byte aligned.
+ */
+#define MOE_MX8_GEMM_MAX_K 8192  /* reduction length of mx4_moe_gemm_mx8 (LDS scale staging) */
+
+int mx8_quantize(const uint16_t* a, const int32_t* live, int64_t rows, int K, uint8_t* q,
+                 uint8_t* s, void* stream);
+
+int mx4_moe_gemm_mx8(const uint8_t* aq, const uint8_t* as, const int32_t* a_row, int64_t a_rows,
+                     const mx4_experts* w, const int32_t* counts, const int32_t* basep, int tile_m,
+                     int64_t mpad_max, int act, float alpha, float limit, void* out,
+                     void* stream);
 
 #define MOE_DECODE_MAX_T 16  /* tokens per mx4_moe_decode call */
 #define MOE_DECODE_MAX_K 8   /* experts per token in mx4_moe_decode */

@@ -19,7 +19,8 @@ MOE_MAX_K, MOE_MAX_E, MOE_MAX_TILE_M = 16, 1024, 256
 
 EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_pack_experts",
            "mx4_moe_gemv", "mx4_moe_gemm", "moe_combine", "mx4_moe_decode", "moe_timing_arm",
-           "moe_timing_read")
+           "moe_timing_read", "mx8_quantize", "mx4_moe_gemm_mx8")
+MOE_MX8_GEMM_MAX_K = 8192
 
 
 class MoeError(RuntimeError):
@@ -69,6 +70,11 @@ def lib() -> ctypes.CDLL:
         L.mx4_moe_decode.restype = ci
         L.mx4_moe_decode.argtypes = [vp, vp, i64, ci, ci, pe, pe, cf, cf,
                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.mx8_quantize.restype = ci
+        L.mx8_quantize.argtypes = [vp, vp, i64, ci, vp, vp, vp]
+        L.mx4_moe_gemm_mx8.restype = ci
+        L.mx4_moe_gemm_mx8.argtypes = [vp, vp, vp, i64, ctypes.POINTER(Mx4ExpertsC), vp, vp, ci,
+                                       i64, ci, cf, cf, vp, vp]
         _lib = L
     return _lib
 
@@ -243,6 +249,43 @@ def mx4_moe_gemm(a, a_row, w, counts, basep, tile_m, mpad_max, act=MOE_ACT_NONE,
                        limit, out, stream)
 
 
+def mx8_quantize(a, live=None, out=None, stream=None):
+    """MXFP8 rows of bf16 rows a [rows][K]: (q u8 [rows][K] E4M3, s u8 [rows][SP] e8m0 with
+    SP = roundup(K/32, 16), padding 0). Rows with live[r] < 0 are left unwritten."""
+    torch = _torch()
+    _check(a, torch.bfloat16, "a")
+    if live is not None:
+        _check(live, torch.int32, "live")
+    rows, K = a.shape
+    if out is None:
+        out = (torch.empty((rows, K), dtype=torch.uint8, device=a.device),
+               torch.empty((rows, scale_row_bytes(K)), dtype=torch.uint8, device=a.device))
+    q, s = out
+    _call("mx8_quantize", _ptr(a), _ptr(live), rows, K, _ptr(q), _ptr(s), _stream(stream))
+    return q, s
+
+
+def mx4_moe_gemm_mx8(aq, as_, a_row, w, counts, basep, tile_m, mpad_max, act=MOE_ACT_NONE,
+                     alpha=1.702, limit=7.0, out=None, stream=None):
+    """mx4_moe_gemm over MXFP8 activation rows (aq, as_) from mx8_quantize."""
+    torch = _torch()
+    _check(aq, torch.uint8, "aq")
+    _check(as_, torch.uint8, "as")
+    if a_row is not None:
+        _check(a_row, torch.int32, "a_row")
+    _check(counts, torch.int32, "counts")
+    _check(basep, torch.int32, "basep")
+    if out is None:
+        if act == MOE_ACT_SWIGLU_OAI:
+            out = torch.empty((mpad_max, w.N // 2), dtype=torch.bfloat16, device=aq.device)
+        else:
+            out = torch.empty((mpad_max, w.N), dtype=torch.float32, device=aq.device)
+    _call("mx4_moe_gemm_mx8", _ptr(aq), _ptr(as_), _ptr(a_row), aq.shape[0], ctypes.byref(w.c),
+          _ptr(counts), _ptr(basep), tile_m, mpad_max, act, float(alpha), float(limit),
+          _ptr(out), _stream(stream))
+    return out
+
+
 def moe_combine(d, pos, w, out=None, stream=None):
     """y f32 [T][D] = slot-order routing-weighted sum of d rows."""
     torch = _torch()
@@ -301,15 +344,30 @@ def moe_timing_read(n: int) -> list:
 def moe_layer(x, logits, gate_up: MX4Experts, down: MX4Experts, k: int, tile_m: int,
               alpha: float = 1.702, limit: float = 7.0, projection: str = "gemm", stream=None):
     """One routed-expert MoE layer: route -> bucket -> gate_up+SwiGLU -> down -> combine.
+    projection: "gemm" or "gemv" (bf16 activations), or "gemm_mx8" (MXFP8 activations on the
+    MX-scaled MFMA: x quantized once, h quantized after the SwiGLU; adds xq/xs/hq/hs).
     Returns a dict of every intermediate (device tensors)."""
+    if projection not in ("gemm", "gemv", "gemm_mx8"):
+        raise ValueError(f"unknown projection {projection!r}")
     T, E = logits.shape
-    fn = mx4_moe_gemm if projection == "gemm" else mx4_moe_gemv
     ids, w = moe_route_topk(logits, k, stream=stream)
     mpad = moe_mpad_max(T, k, E, tile_m)
     counts, basep, row_tok, pos = moe_bucket(ids, E, tile_m, mpad, stream=stream)
-    h = fn(x, row_tok, gate_up, counts, basep, tile_m, mpad, MOE_ACT_SWIGLU_OAI, alpha, limit,
-           stream=stream)
-    d = fn(h, None, down, counts, basep, tile_m, mpad, MOE_ACT_NONE, alpha, limit, stream=stream)
+    extra = {}
+    if projection == "gemm_mx8":
+        xq, xs = mx8_quantize(x, stream=stream)
+        h = mx4_moe_gemm_mx8(xq, xs, row_tok, gate_up, counts, basep, tile_m, mpad,
+                             MOE_ACT_SWIGLU_OAI, alpha, limit, stream=stream)
+        hq, hs = mx8_quantize(h, live=row_tok, stream=stream)
+        d = mx4_moe_gemm_mx8(hq, hs, None, down, counts, basep, tile_m, mpad, MOE_ACT_NONE,
+                             alpha, limit, stream=stream)
+        extra = {"xq": xq, "xs": xs, "hq": hq, "hs": hs}
+    else:
+        fn = mx4_moe_gemm if projection == "gemm" else mx4_moe_gemv
+        h = fn(x, row_tok, gate_up, counts, basep, tile_m, mpad, MOE_ACT_SWIGLU_OAI, alpha,
+               limit, stream=stream)
+        d = fn(h, None, down, counts, basep, tile_m, mpad, MOE_ACT_NONE, alpha, limit,
+               stream=stream)
     y = moe_combine(d, pos, w, stream=stream)
     return {"ids": ids, "w": w, "mpad": mpad, "counts": counts, "basep": basep,
-            "row_tok": row_tok, "pos": pos, "h": h, "d": d, "y": y}
+            "row_tok": row_tok, "pos": pos, "h": h, "d": d, "y": y, **extra}

@@ -9,9 +9,14 @@ int moe_launch_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, con
                     const int32_t* counts, const int32_t* basep, int tile_m, int64_t mpad_max,
                     int act, float alpha, float limit, void* out, hipStream_t stream);
 
+int moe_launch_gemm_mx8(const uint8_t* aq, const uint8_t* as, const int32_t* a_row,
+                        int64_t a_rows, const mx4_experts* w, const int32_t* counts,
+                        const int32_t* basep, int tile_m, int64_t mpad_max, int act, float alpha,
+                        float limit, void* out, hipStream_t stream);
+
 namespace {
 
-int check_projection(const uint16_t* a, const int32_t* a_row, int64_t a_rows,
+int check_projection(const void* a, const int32_t* a_row, int64_t a_rows,
                      const mx4_experts* w, const int32_t* counts, const int32_t* basep,
                      int tile_m, int64_t mpad_max, int act, void* out) {
   if (!a || !w || !w->q || !w->s || !counts || !basep || !out) return MOE_EINVAL;
@@ -59,4 +64,17 @@ extern "C" int mx4_moe_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_r
   if (st != MOE_OK) return st;
   return moe_launch_gemm(a, a_row, a_rows, w, counts, basep, tile_m, mpad_max, act, alpha, limit, out,
                          (hipStream_t)stream);
+}
+
+extern "C" int mx4_moe_gemm_mx8(const uint8_t* aq, const uint8_t* as, const int32_t* a_row,
+                                int64_t a_rows, const mx4_experts* w, const int32_t* counts,
+                                const int32_t* basep, int tile_m, int64_t mpad_max, int act,
+                                float alpha, float limit, void* out, void* stream) {
+  if (!as) return MOE_EINVAL;
+  const int st = check_projection(aq, a_row, a_rows, w, counts, basep, tile_m, mpad_max, act, out);
+  if (st != MOE_OK) return st;
+  if (w->K > MOE_MX8_GEMM_MAX_K) return MOE_ESHAPE;
+  if (((uintptr_t)as) & 15) return MOE_EALIGN;
+  return moe_launch_gemm_mx8(aq, as, a_row, a_rows, w, counts, basep, tile_m, mpad_max, act, alpha,
+                             limit, out, (hipStream_t)stream);
 }

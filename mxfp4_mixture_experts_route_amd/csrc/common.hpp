@@ -12,6 +12,11 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// operand formats of v_mfma_scale_f32_*_f8f6f4 (the cbsz / blgp fields)
+constexpr int kMfmaFmtFp8 = 0;   // E4M3
+constexpr int kMfmaFmtFp4 = 4;   // E2M1
 
 constexpr int kWave = 64;
 constexpr int kChunkBlocks = 4;   // MX blocks per chunk of the chunked weight layout

@@ -1,4 +1,5 @@
-// mx4_moe_gemm: routed-expert MXFP4 projection for prefill, on bf16 MFMA with fp32 accumulation.
+// mx4_moe_gemm: routed-expert MXFP4 projection for prefill, on bf16 MFMA with fp32 accumulation;
+// mx4_moe_gemm_mx8: the same pipeline over MXFP8 activation rows, on the MX-scaled MFMA.
 //
 // Sources: PR #3579 "dasLLAMA gpt-oss arc", Metal fusion-lane commit (the grouped expert matmul
 // over the buckets starts its accumulator tiles from the expert's bias row instead of running a
@@ -43,6 +44,14 @@
 //    never computed; rows past the count are never stored. Experts with no rows exit at once.
 //  * SwiGLU mode pairs gate tiles with the matching up tiles in the same wavefront, so the
 //    epilogue is register-local and only bf16 h leaves the kernel.
+//  * MXFP8 variant: activation rows are E4M3 bytes (128 B per row per chunk, swizzled over 8
+//    pieces by gemm_swz8) and v_mfma_scale_f32_16x16x128_f8f6f4 takes the lane's 16-byte MX
+//    block unchanged as its A operand (32 e2m1 values: weight row lr, block 4c + lg), with the
+//    block's e8m0 byte as the A scale, so nothing is decoded in registers. Its B operand holds
+//    k 16*lg..16*lg+15 and 64+16*lg..64+16*lg+15 of the token column (the instruction's operand
+//    layout on gfx950, established by a one-wavefront layout check against the exact product),
+//    and the B scale is the activation block's e8m0 byte, from the pass's scale rows staged in
+//    LDS. One MFMA per weight tile, token tile and chunk replaces 4 bf16 MFMAs and 4 converts.
 #include "gemv_core.hpp"
 #include "launch.hpp"
 
@@ -57,25 +66,41 @@ constexpr int kGmMaxWT = 3;              // weight tiles (16 rows each) per wave
 __host__ __device__ constexpr int gemm_wt(int act) { return act == MOE_ACT_SWIGLU_OAI ? 2 : 3; }
 constexpr int kGmTT = 8;                 // token tiles (16 rows each) per pass: 128 routed rows
 constexpr int kGmChunkK = 128;           // k per chunk = 4 MX blocks
-constexpr int kGmRowBytes = kGmChunkK * 2;   // activation bytes per row per chunk
+// activation bytes per row per chunk: bf16 rows, or MXFP8 rows (E4M3 bytes; their e8m0 scales
+// are staged separately, once per pass)
+__host__ __device__ constexpr int gemm_row_bytes(bool mx8) { return mx8 ? kGmChunkK : 2 * kGmChunkK; }
 
 // weight chunks in flight (register ring slots): 4 with 2 tiles per wavefront, 3 with 3 tiles
 // (registers); the activation chunks are issued 3 ahead either way
 __host__ __device__ constexpr int gemm_wring(int wt) { return wt == 2 ? 4 : 3; }
 constexpr int kGmXRing = 4;              // activation chunk buffers in LDS (3 chunks ahead)
-// LDS of a pass with NTT token tiles
-__host__ __device__ constexpr int gemm_buf_bytes(int ntt) { return ntt * 16 * kGmRowBytes; }
-// after the activation ring: 1 KB that the DMA of wavefronts without a share of a chunk writes
-constexpr int kGmDummyOff = kGmXRing * gemm_buf_bytes(kGmTT);
-constexpr int kGmLdsBytes = kGmDummyOff + 1024;
+// LDS of one activation chunk of a pass with NTT token tiles
+__host__ __device__ constexpr int gemm_buf_bytes(int ntt, bool mx8) {
+  return ntt * 16 * gemm_row_bytes(mx8);
+}
+// after the activation ring: 1 KB that the DMA of wavefronts without a share of a chunk writes;
+// MXFP8 passes then stage the e8m0 scale rows of their 128 routed rows
+__host__ __device__ constexpr int gemm_dummy_off(bool mx8) {
+  return kGmXRing * gemm_buf_bytes(kGmTT, mx8);
+}
+// LDS pitch of a staged scale row: fixed, so that a token tile's offset is an immediate
+constexpr int kGmScalePitch = MOE_MX8_GEMM_MAX_K / 32;
+__host__ __device__ constexpr int gemm_lds_bytes(bool mx8) {
+  return gemm_dummy_off(mx8) + 1024 + (mx8 ? kGmTT * 16 * kGmScalePitch : 0);
+}
+// 16-byte piece q of routed row m of an MXFP8 chunk sits at slot q ^ gemm_swz8(m) of the row's
+// 128 bytes: the B-fragment reads of 16 consecutive rows at one q then touch 16 different
+// 16-byte bank groups (8 different ones for rows m and m + 8 apart in the low bit)
+__device__ __forceinline__ int gemm_swz8(int m) { return (m & 7) ^ ((m >> 3) & 1); }
 
 // Everything one pass over up to 16*NTT routed rows of one expert needs.
 struct GemmCtx {
   const int32_t* a_row;
   const float* bias;
   void* out;
-  __amdgpu_buffer_rsrc_t rq, rs, ra;
-  int e, N, K, C, klast, row0, p0, live, F;
+  const uint8_t* a_scale;   // MXFP8 activation scale rows (pitch spa), else unused
+  __amdgpu_buffer_rsrc_t rq, rs, ra, ras;
+  int e, N, K, KB, C, klast, row0, p0, live, F, spa;
   int tid, lr, lg;
   float alpha, limit;
   int tile_base[kGmMaxWT];
@@ -84,22 +109,27 @@ struct GemmCtx {
 };
 
 // One pass with NTT live token tiles (compile-time, so the MFMA loop is straight-line code and
-// LDS reads can be scheduled ahead of the MFMAs that use them).
-template <int ACT, int NTT>
+// LDS reads can be scheduled ahead of the MFMAs that use them). MX8: MXFP8 activations on the
+// MX-scaled MFMA, else bf16 activations on bf16 MFMA.
+template <int ACT, int NTT, bool MX8>
 __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict__ xs) {
   constexpr bool swiglu = (ACT == MOE_ACT_SWIGLU_OAI);
   constexpr int kGmWT = gemm_wt(ACT);
-  constexpr int BUF = gemm_buf_bytes(NTT);
-  // DMA instructions per wavefront per chunk: the chunk's NTT*4 KB split over the wavefronts,
+  constexpr int ROWB = gemm_row_bytes(MX8);
+  constexpr int PIECES = ROWB / 16;          // 16-byte pieces per row per chunk
+  constexpr int BUF = gemm_buf_bytes(NTT, MX8);
+  constexpr int KBS = BUF / 1024;            // 1 KB DMA instructions per chunk
+  // DMA instructions per wavefront per chunk: the chunk's KBS KB split over the wavefronts,
   // every wavefront issuing the same count (surplus ones copy zeros into a dummy KB) so that
   // the vector-memory counter waits below are exact for each of them
-  constexpr int NX = (NTT * 4 + kGmWaves - 1) / kGmWaves;
+  constexpr int NX = (KBS + kGmWaves - 1) / kGmWaves;
   constexpr int LOADS = NX + 2 * kGmWT;   // vector-memory instructions per wavefront per chunk
   static_assert(2 * kGmWT + 2 * LOADS <= 63, "vmcnt range");
   const int C = g.C;
   const int lr = g.lr, lg = g.lg;
   const int lane = g.tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(g.tid >> 6);   // uniform: LDS-DMA base
+  const int dummy = gemm_dummy_off(MX8);
 
   // weight fetch of chunk c into a ring slot. Chunks past K re-read the last chunk (their
   // compute is skipped), so every chunk issues the same loads and only the last one differs
@@ -117,31 +147,34 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
   };
 
   // activation DMA: instruction i of this wavefront covers 16-byte slots p = j*64 + lane,
-  // j = wave + 4*i, i.e. routed row m = p / 16 of the pass and swizzled slot p % 16, which holds
-  // the row's 16-byte piece q = (p % 16) ^ (m % 16) of the chunk
+  // j = wave + 8*i, i.e. routed row m = p / PIECES of the pass and swizzled slot p % PIECES,
+  // which holds the row's piece q = (p % PIECES) ^ swz(m) of the chunk (bf16: swz = m % 16;
+  // MXFP8: gemm_swz8)
   uint32_t xo[NX], xol[NX];
 #pragma unroll
   for (int i = 0; i < NX; ++i) {
     const int p = (wave + kGmWaves * i) * 64 + lane;
-    const int m = p >> 4, q = (p & 15) ^ (m & 15);
+    const int m = p / PIECES;
+    const int q = (p % PIECES) ^ (MX8 ? gemm_swz8(m) : (m & 15));
     uint32_t off = kOOB;
-    if (m < g.live && wave + kGmWaves * i < NTT * 4) {
+    if (m < g.live && wave + kGmWaves * i < KBS) {
       const int r = g.row0 + g.p0 + m;
       const uint32_t src = g.a_row ? (uint32_t)g.a_row[r] : (uint32_t)r;
-      off = src * (uint32_t)g.K * 2 + q * 16;
+      off = src * (uint32_t)g.K * (MX8 ? 1u : 2u) + q * 16;
     }
     xo[i] = off;
-    xol[i] = (q * 8 < g.klast) ? off : kOOB;   // the last chunk may be narrower than 128 k
+    // the last chunk may be narrower than 128 k
+    xol[i] = (q * 16 < g.klast * (MX8 ? 1 : 2)) ? off : kOOB;
   }
   auto load_x = [&](int c) {
     const int cc = min(c, C - 1);
     const bool last = cc == C - 1;
     const int dst = (c % kGmXRing) * BUF;
-    const uint32_t ck = (uint32_t)cc * kGmRowBytes;
+    const uint32_t ck = (uint32_t)cc * ROWB;
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int j = wave + kGmWaves * i;   // uniform
-      const int d = j < NTT * 4 ? dst + j * 1024 : kGmDummyOff;
+      const int d = j < KBS ? dst + j * 1024 : dummy;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           g.ra, (__attribute__((address_space(3))) void*)(xs + d), 16, last ? xol[i] : xo[i], ck,
           0, 0);
@@ -166,6 +199,26 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
   uint32_t wx[kGmWRing][kGmWT];
 
   __syncthreads();  // the previous pass is done with the LDS buffers
+  // MXFP8: the e8m0 scale rows of the pass's routed rows, row m at xsc + m * kGmScalePitch
+  // (the bytes past the row's spa read as zeros), by LDS-DMA ahead of everything else: one
+  // instruction per 4 rows. The first wait of the K loop covers them (loads complete in issue
+  // order).
+  uint8_t* const xsc = xs + dummy + 1024;
+  if (MX8) {
+    constexpr int kRowsPerKB = 1024 / kGmScalePitch;
+    for (int j = wave; j < NTT * 16 / kRowsPerKB; j += kGmWaves) {
+      const int m = j * kRowsPerKB + lane / (kGmScalePitch / 16);
+      const int piece = lane % (kGmScalePitch / 16);
+      uint32_t off = kOOB;
+      if (m < g.live && piece * 16 < g.spa) {
+        const int r = g.row0 + g.p0 + m;
+        const uint32_t src = g.a_row ? (uint32_t)g.a_row[r] : (uint32_t)r;
+        off = src * (uint32_t)g.spa + piece * 16;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          g.ras, (__attribute__((address_space(3))) void*)(xsc + j * 1024), 16, off, 0, 0, 0);
+    }
+  }
   // prologue, in the steady state's issue order (W0 X0 W1 X1 W2 X2 W3 with a ring of 4;
   // X0 W0 X1 W1 X2 W2 with a ring of 3)
 #pragma unroll
@@ -184,6 +237,7 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
     }
   }
 
+  const int swz = MX8 ? gemm_swz8(lr) : lr;   // m % 16 == lr for every token tile
   for (int c0 = 0; c0 < C; c0 += kGmWRing) {
 #pragma unroll
     for (int sl = 0; sl < kGmWRing; ++sl) {
@@ -203,22 +257,64 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
       __builtin_amdgcn_sched_barrier(0);
       if (c < C) {
         const uint8_t* xb = xs + (c % kGmXRing) * BUF;
-        float cs[kGmWT];
+        if constexpr (MX8) {
+          // v_mfma_scale_f32_16x16x128_f8f6f4: A = the lane's 16-byte MX block as 32 e2m1
+          // values (weight row lr, block 4c + lg) with its e8m0 byte as scale; B = 32 E4M3
+          // values of token column lr: k 16*lg..16*lg+15 and 64+16*lg..64+16*lg+15 of the
+          // chunk, with the scale of block 4c + lg. Blocks past K take scale 0 (their data
+          // are zeros) so that no padding byte can inject a NaN scale.
+          const bool kb_live = 4 * c + lg < g.KB;
+          int sa[kGmWT];
 #pragma unroll
-        for (int t = 0; t < kGmWT; ++t) cs[t] = e8m0_scale_operand(wx[sl][t]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16x8_t A[kGmWT];
-#pragma unroll
-          for (int t = 0; t < kGmWT; ++t) A[t] = dequant8(wq[sl][t][i], cs[t]);
+          for (int t = 0; t < kGmWT; ++t) sa[t] = kb_live ? (int)wx[sl][t] : 0;
+          // B fragments of token tile tt + 1 are read from LDS while tile tt's MFMAs run (one
+          // tile ahead, not all of them: 8 tiles of 9 VGPRs would not fit beside the ring)
+          // per-lane bases; a token tile adds a constant (an instruction offset)
+          const uint8_t* xb0 = xb + lr * ROWB + ((lg ^ swz) << 4);
+          const uint8_t* xb1 = xb + lr * ROWB + (((4 + lg) ^ swz) << 4);
+          const uint8_t* sbp = xsc + lr * kGmScalePitch + 4 * c + lg;
+          auto read_b = [&](int tt, i32x8_t& B, int& sb) {
+            const u32x4_t b0 = *reinterpret_cast<const u32x4_t*>(xb0 + tt * 16 * ROWB);
+            const u32x4_t b1 = *reinterpret_cast<const u32x4_t*>(xb1 + tt * 16 * ROWB);
+            sb = kb_live ? (int)sbp[tt * 16 * kGmScalePitch] : 0;
+            B = i32x8_t{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                        (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+          };
+          i32x8_t Bn;
+          int sbn;
+          read_b(0, Bn, sbn);
 #pragma unroll
           for (int tt = 0; tt < NTT; ++tt) {
-            const int m = tt * 16 + lr;   // m % 16 == lr
-            const bf16x8_t B =
-                *reinterpret_cast<const bf16x8_t*>(xb + (m * 16 + ((lg * 4 + i) ^ lr)) * 16);
+            const i32x8_t B = Bn;
+            const int sb = sbn;
+            if (tt + 1 < NTT) read_b(tt + 1, Bn, sbn);
 #pragma unroll
-            for (int t = 0; t < kGmWT; ++t)
-              acc[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t], B, acc[t][tt], 0, 0, 0);
+            for (int t = 0; t < kGmWT; ++t) {
+              const i32x8_t A = {(int)wq[sl][t][0], (int)wq[sl][t][1], (int)wq[sl][t][2],
+                                 (int)wq[sl][t][3], 0, 0, 0, 0};
+              acc[t][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  A, B, acc[t][tt], kMfmaFmtFp4, kMfmaFmtFp8, 0, sa[t], 0, sb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          float cs[kGmWT];
+#pragma unroll
+          for (int t = 0; t < kGmWT; ++t) cs[t] = e8m0_scale_operand(wx[sl][t]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bf16x8_t A[kGmWT];
+#pragma unroll
+            for (int t = 0; t < kGmWT; ++t) A[t] = dequant8(wq[sl][t][i], cs[t]);
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+              const int m = tt * 16 + lr;   // m % 16 == lr
+              const bf16x8_t B =
+                  *reinterpret_cast<const bf16x8_t*>(xb + (m * 16 + ((lg * 4 + i) ^ swz)) * 16);
+#pragma unroll
+              for (int t = 0; t < kGmWT; ++t)
+                acc[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t], B, acc[t][tt], 0, 0, 0);
+            }
           }
         }
       }
@@ -268,13 +364,13 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
   }
 }
 
-template <int ACT>
+template <int ACT, bool MX8>
 __global__ void __launch_bounds__(kGmThreads)
-gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, int a_rows,
-            const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
-            const float* __restrict__ bias, const int32_t* __restrict__ counts,
-            const int32_t* __restrict__ basep, int E, int N, int K, float alpha, float limit,
-            void* __restrict__ out) {
+gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int a_rows,
+            const int32_t* __restrict__ a_row, const uint8_t* __restrict__ q,
+            const uint8_t* __restrict__ s, const float* __restrict__ bias,
+            const int32_t* __restrict__ counts, const int32_t* __restrict__ basep, int E, int N,
+            int K, float alpha, float limit, void* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   const int c64 = ((int)(threadIdx.x & 63) < E) ? counts[threadIdx.x & 63] : 0;
   const int e = wave_slot_expert(counts, E, (int)blockIdx.y, c64);
@@ -284,6 +380,7 @@ gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
   g.a_row = a_row;
   g.bias = bias;
   g.out = out;
+  g.a_scale = a_scale;
   g.e = e;
   g.N = N;
   g.K = K;
@@ -291,6 +388,7 @@ gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
   g.limit = limit;
   g.F = N >> 1;
   const int KB = K >> 5;
+  g.KB = KB;
   g.C = (KB + kChunkBlocks - 1) / kChunkBlocks;             // chunks of 4 blocks
   const int wlast = KB - (g.C - 1) * kChunkBlocks;          // blocks in the last chunk
   g.klast = K - (g.C - 1) * kGmChunkK;                      // k in the last chunk
@@ -318,9 +416,11 @@ gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
   // buffer resources: this expert's nibbles and scales, and the activation rows
   const size_t ebase = (size_t)e * N * KB;   // first block of this expert (chunked layout)
   const int SP = scale_row_bytes(KB);        // scale row pitch (padding reads as 0)
+  g.spa = SP;                                // MXFP8 activation scale rows use the same pitch
   g.rq = make_rsrc(q + 16 * ebase, (uint32_t)N * KB * 16);
   g.rs = make_rsrc(s + (size_t)e * N * SP, (uint32_t)N * SP);
-  g.ra = make_rsrc(a, (uint32_t)a_rows * K * 2);
+  g.ra = make_rsrc(a, (uint32_t)a_rows * K * (MX8 ? 1 : 2));
+  g.ras = make_rsrc(a_scale, MX8 ? (uint32_t)a_rows * SP : 0u);
 
   // per-lane offsets of the lane's block in a full chunk and in the (narrower) last chunk
 #pragma unroll
@@ -336,16 +436,56 @@ gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
     g.p0 = p0;
     g.live = min(kGmTT * 16, cnt - p0);
     switch ((g.live + 15) >> 4) {
-      case 1: gemm_pass<ACT, 1>(g, xs); break;
-      case 2: gemm_pass<ACT, 2>(g, xs); break;
-      case 3: gemm_pass<ACT, 3>(g, xs); break;
-      case 4: gemm_pass<ACT, 4>(g, xs); break;
-      case 5: gemm_pass<ACT, 5>(g, xs); break;
-      case 6: gemm_pass<ACT, 6>(g, xs); break;
-      case 7: gemm_pass<ACT, 7>(g, xs); break;
-      default: gemm_pass<ACT, 8>(g, xs); break;
+      case 1: gemm_pass<ACT, 1, MX8>(g, xs); break;
+      case 2: gemm_pass<ACT, 2, MX8>(g, xs); break;
+      case 3: gemm_pass<ACT, 3, MX8>(g, xs); break;
+      case 4: gemm_pass<ACT, 4, MX8>(g, xs); break;
+      case 5: gemm_pass<ACT, 5, MX8>(g, xs); break;
+      case 6: gemm_pass<ACT, 6, MX8>(g, xs); break;
+      case 7: gemm_pass<ACT, 7, MX8>(g, xs); break;
+      default: gemm_pass<ACT, 8, MX8>(g, xs); break;
     }
   }
+}
+
+// Grid and launch of either variant: x = weight-row slices of 128 (SwiGLU) or 384 rows,
+// y = expert slots (live experts in id order; slots past the live ones exit at once).
+template <bool MX8>
+int gemm_launch(const void* a, const uint8_t* a_scale, const int32_t* a_row, int64_t a_rows,
+                const mx4_experts* w, const int32_t* counts, const int32_t* basep, int tile_m,
+                int64_t mpad_max, int act, float alpha, float limit, void* out,
+                hipStream_t stream) {
+  // buffer resources address at most 2 GB: one expert's weights and the activation matrix
+  if ((int64_t)w->N * w->K / 2 >= (1LL << 31) ||
+      a_rows * w->K * (MX8 ? 1 : 2) >= (1LL << 31) ||
+      a_rows * scale_row_bytes(w->K / 32) >= (1LL << 31))
+    return MOE_ESHAPE;
+  const int64_t rows_per_wg = 16 * kGmWaves * gemm_wt(MOE_ACT_NONE);
+  const int64_t bx = (act == MOE_ACT_SWIGLU_OAI) ? (w->N / 2 + 127) / 128
+                                                 : (w->N + rows_per_wg - 1) / rows_per_wg;
+  int64_t slots = mpad_max / tile_m;
+  if (slots > w->E) slots = w->E;
+  // > 64 KB of dynamic LDS must be opted into, once per kernel, at the largest size used
+  static bool lds_attr_set = false;
+  const int lds_max = gemm_lds_bytes(MX8);
+  if (!lds_attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MOE_ACT_NONE, MX8>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds_max) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MOE_ACT_SWIGLU_OAI, MX8>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds_max) != hipSuccess)
+      return MOE_ELAUNCH;
+    lds_attr_set = true;
+  }
+  const int lds = gemm_lds_bytes(MX8);
+  const dim3 grid((unsigned)bx, (unsigned)slots), block(kGmThreads);
+  if (act == MOE_ACT_SWIGLU_OAI)
+    launch(gemm_kernel<MOE_ACT_SWIGLU_OAI, MX8>, grid, block, lds, stream, a, a_scale,
+           (int)a_rows, a_row, w->q, w->s, w->bias, counts, basep, w->E, w->N, w->K, alpha,
+           limit, out);
+  else
+    launch(gemm_kernel<MOE_ACT_NONE, MX8>, grid, block, lds, stream, a, a_scale, (int)a_rows,
+           a_row, w->q, w->s, w->bias, counts, basep, w->E, w->N, w->K, alpha, limit, out);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
 }  // namespace moe
@@ -353,32 +493,14 @@ gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_row, i
 int moe_launch_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const mx4_experts* w,
                     const int32_t* counts, const int32_t* basep, int tile_m, int64_t mpad_max,
                     int act, float alpha, float limit, void* out, hipStream_t stream) {
-  // buffer resources address at most 2 GB: one expert's weights and the activation matrix
-  if ((int64_t)w->N * w->K / 2 >= (1LL << 31) || a_rows * w->K * 2 >= (1LL << 31))
-    return MOE_ESHAPE;
-  const int64_t rows_per_wg = 16 * moe::kGmWaves * moe::gemm_wt(MOE_ACT_NONE);
-  const int64_t bx = (act == MOE_ACT_SWIGLU_OAI) ? (w->N / 2 + 127) / 128
-                                                 : (w->N + rows_per_wg - 1) / rows_per_wg;
-  int64_t slots = mpad_max / tile_m;
-  if (slots > w->E) slots = w->E;
-  static bool lds_attr_set = false;  // > 64 KB of dynamic LDS must be opted into once
-  if (!lds_attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::gemm_kernel<MOE_ACT_NONE>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            moe::kGmLdsBytes) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::gemm_kernel<MOE_ACT_SWIGLU_OAI>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            moe::kGmLdsBytes) != hipSuccess)
-      return MOE_ELAUNCH;
-    lds_attr_set = true;
-  }
-  if (act == MOE_ACT_SWIGLU_OAI)
-    moe::launch(moe::gemm_kernel<MOE_ACT_SWIGLU_OAI>, dim3((unsigned)bx, (unsigned)slots),
-                       dim3(moe::kGmThreads), moe::kGmLdsBytes, stream, a, a_row, (int)a_rows,
-                       w->q, w->s, w->bias, counts, basep, w->E, w->N, w->K, alpha, limit, out);
-  else
-    moe::launch(moe::gemm_kernel<MOE_ACT_NONE>, dim3((unsigned)bx, (unsigned)slots),
-                       dim3(moe::kGmThreads), moe::kGmLdsBytes, stream, a, a_row, (int)a_rows,
-                       w->q, w->s, w->bias, counts, basep, w->E, w->N, w->K, alpha, limit, out);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+  return moe::gemm_launch<false>(a, nullptr, a_row, a_rows, w, counts, basep, tile_m, mpad_max,
+                                 act, alpha, limit, out, stream);
+}
+
+int moe_launch_gemm_mx8(const uint8_t* aq, const uint8_t* as, const int32_t* a_row,
+                        int64_t a_rows, const mx4_experts* w, const int32_t* counts,
+                        const int32_t* basep, int tile_m, int64_t mpad_max, int act, float alpha,
+                        float limit, void* out, hipStream_t stream) {
+  return moe::gemm_launch<true>(aq, as, a_row, a_rows, w, counts, basep, tile_m, mpad_max, act,
+                                alpha, limit, out, stream);
 }

@@ -167,3 +167,45 @@ def test_timing_argument_checks():
     assert L.moe_timing_read(buf, -1) == _lib.MOE_EINVAL
     assert L.moe_timing_read(buf, 1) == _lib.MOE_ESHAPE       # nothing was timed
     assert L.moe_timing_read(buf, 0) == _lib.MOE_OK
+
+
+@no_gpu
+def test_mx8_quantize_argument_checks():
+    L = _lib.lib()
+    q = L.mx8_quantize
+    assert q(None, None, 4, 64, FAKE, FAKE, None) == _lib.MOE_EINVAL
+    assert q(FAKE, None, 0, 64, FAKE, FAKE, None) == _lib.MOE_EINVAL
+    assert q(FAKE, None, 4, 64, None, FAKE, None) == _lib.MOE_EINVAL
+    assert q(FAKE, None, 4, 64, FAKE, None, None) == _lib.MOE_EINVAL
+    assert q(FAKE, None, 4, 48, FAKE, FAKE, None) == _lib.MOE_ESHAPE
+    assert q(FAKE, None, 4, 16, FAKE, FAKE, None) == _lib.MOE_ESHAPE
+    assert q(FAKE, None, 1 << 20, 4096, FAKE, FAKE, None) == _lib.MOE_ESHAPE   # rows*K >= 2^31
+    assert q(ctypes.c_void_p(0x1008), None, 4, 64, FAKE, FAKE, None) == _lib.MOE_EALIGN
+    assert q(FAKE, None, 4, 64, ctypes.c_void_p(0x1004), FAKE, None) == _lib.MOE_EALIGN
+    assert q(FAKE, None, 4, 64, FAKE, ctypes.c_void_p(0x1001), None) == _lib.MOE_EALIGN
+
+
+@no_gpu
+def test_gemm_mx8_argument_checks():
+    f = _lib.lib().mx4_moe_gemm_mx8
+    good = experts()
+    NONE, SW = _lib.MOE_ACT_NONE, _lib.MOE_ACT_SWIGLU_OAI
+
+    def call(aq=FAKE, as_=FAKE, a_row=FAKE, a_rows=8, w=good, counts=FAKE, basep=FAKE,
+             tile_m=16, mpad=64, act=NONE, out=FAKE):
+        return f(aq, as_, a_row, a_rows, None if w is None else ctypes.byref(w), counts, basep,
+                 tile_m, mpad, act, 1.702, 7.0, out, None)
+
+    assert call(aq=None) == _lib.MOE_EINVAL
+    assert call(as_=None) == _lib.MOE_EINVAL
+    assert call(w=None) == _lib.MOE_EINVAL
+    assert call(counts=None) == _lib.MOE_EINVAL
+    assert call(act=7) == _lib.MOE_EINVAL
+    assert call(w=experts(K=48)) == _lib.MOE_ESHAPE
+    assert call(w=experts(K=_lib.MOE_MX8_GEMM_MAX_K + 32)) == _lib.MOE_ESHAPE
+    assert call(w=experts(N=63), act=SW) == _lib.MOE_ESHAPE
+    assert call(tile_m=0) == _lib.MOE_ESHAPE
+    assert call(a_row=None, a_rows=8, mpad=64) == _lib.MOE_ESHAPE
+    assert call(aq=ctypes.c_void_p(0x1008)) == _lib.MOE_EALIGN
+    assert call(as_=ctypes.c_void_p(0x1008)) == _lib.MOE_EALIGN
+    assert call(out=ctypes.c_void_p(0x1002)) == _lib.MOE_EALIGN
