@@ -11,8 +11,9 @@ GEMV, GEMV, combine) is timed beside it.
 
 Prints ONE JSON line. `value` = decode tokens/s through the 24-layer stack. The same line also
 carries the dominant kernel's roofline, the decode weight GB/s of the two MXFP4 projections, the
-pp512 prefill expert-GEMM TFLOP/s (gpt-oss-20b shape, T=512, bf16 MFMA), and the CPU oracle timed
-on a bounded sample of the decode workload on the host cores. Kernel durations come from the
+pp512 prefill expert-GEMM TFLOP/s (gpt-oss-20b shape, T=512, bf16 MFMA, and beside it the same
+layers with MXFP8 activations on the MX-scaled MFMA), and the CPU oracle timed on a bounded sample
+of the decode workload on the host cores. Kernel durations come from the
 library's kernel timing (moe_timing_arm: HIP events the runtime stamps at each kernel's own start
 and end, on the stream it runs on), the interval a rocprofv3 kernel trace reports.
 
@@ -29,6 +30,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_DENSE_TFLOPS = 2500.0      # MI355X bf16 dense MFMA
+FP8_DENSE_TFLOPS = 5000.0       # MI355X fp8 dense MFMA (the rate of an fp4 x fp8 MX product)
 
 
 def parse_args():
@@ -97,6 +99,27 @@ class Layer:
         self.route_bucket()
         self.gate_up()
         self.down()
+        self.combine()
+
+    def alloc_mx8(self, torch):
+        """MXFP8 copies of x and h for chain_mx8."""
+        u8, sp, wl = torch.uint8, self.moe.scale_row_bytes, self.wl
+        self.xq = torch.empty((wl.T, wl.dim), dtype=u8, device="cuda")
+        self.xs = torch.empty((wl.T, sp(wl.dim)), dtype=u8, device="cuda")
+        self.hq = torch.empty((self.mpad, wl.ffn), dtype=u8, device="cuda")
+        self.hs = torch.empty((self.mpad, sp(wl.ffn)), dtype=u8, device="cuda")
+
+    def chain_mx8(self):
+        """The chain with MXFP8 activations: route, bucket, quantize x, gate_up (MX MFMA),
+        quantize h, down (MX MFMA), combine (7 launches)."""
+        m, wl, c = self.moe, self.wl, self.csr
+        self.route_bucket()
+        m.mx8_quantize(self.x, out=(self.xq, self.xs))
+        m.mx4_moe_gemm_mx8(self.xq, self.xs, c[2], self.GU, c[0], c[1], wl.tile_m, self.mpad,
+                           m.MOE_ACT_SWIGLU_OAI, 1.702, 7.0, out=self.h)
+        m.mx8_quantize(self.h, live=c[2], out=(self.hq, self.hs))
+        m.mx4_moe_gemm_mx8(self.hq, self.hs, None, self.DN, c[0], c[1], wl.tile_m, self.mpad,
+                           m.MOE_ACT_NONE, 1.702, 7.0, out=self.d)
         self.combine()
 
     def decode(self):
@@ -357,6 +380,23 @@ def main():
             "chain_tokens_per_s": round(pw.T * pw.layers * p_steps / psecs, 1),
             "per_layer_chain_us": round(1e6 * psecs / (p_steps * pw.layers), 2),
             "flops_per_layer": flops,
+        }
+        log("pp512 with MXFP8 activations (MX-scaled MFMA)")
+        for L in players:
+            L.alloc_mx8(torch)
+        msecs, _ = graph_time(torch, lambda: [L.chain_mx8() for L in players], p_steps,
+                              args.warmup)
+        mkt = kernel_times_us(moe, torch, players, lambda L: L.chain_mx8(), 7, args.kernel_reps,
+                              sleep_cycles)
+        mx_tflops = flops / ((mkt[3] + mkt[5]) * 1e-6) / 1e12
+        result["prefill_pp512"]["mx8"] = {
+            "activations": "MXFP8 (E4M3 + e8m0 per 32), v_mfma_scale_f32_16x16x128_f8f6f4",
+            "expert_gemm_TFLOPs": round(mx_tflops, 1),
+            "frac_fp8_peak": round(mx_tflops / FP8_DENSE_TFLOPS, 4),
+            "gate_up_us": round(mkt[3], 2), "down_us": round(mkt[5], 2),
+            "quantize_x_us": round(mkt[2], 2), "quantize_h_us": round(mkt[4], 2),
+            "chain_tokens_per_s": round(pw.T * pw.layers * p_steps / msecs, 1),
+            "per_layer_chain_us": round(1e6 * msecs / (p_steps * pw.layers), 2),
         }
         del players
         torch.cuda.empty_cache()
