@@ -42,6 +42,15 @@ __device__ __forceinline__ uint32_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
 }
 
+// Keeps the memory operations before and after it in program order: an empty asm statement
+// that clobbers memory stops IR passes from sinking or hoisting loads across it, and the
+// scheduling barrier stops the machine scheduler. Vector loads complete in issue order, so the
+// compiler's own wait counts depend on that order.
+__device__ __forceinline__ void issue_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n (<= 63) vector-memory
 // operations of this wavefront are outstanding, and for nothing else.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }

@@ -221,24 +221,31 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
   }
   // prologue, in the steady state's issue order (W0 X0 W1 X1 W2 X2 W3 with a ring of 4;
   // X0 W0 X1 W1 X2 W2 with a ring of 3)
+  // (issue_fence, not only a scheduling barrier: the plain weight loads would otherwise sink
+  // below the DMA copies, and the compiler's wait before the first MFMAs, merged into the loop
+  // header, would then hold every later chunk for a younger load than it needs)
+  issue_fence();
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     if (kGmWRing == 4 && c < kGmWRing) {
       load_w(c, wq[c], wx[c]);
-      __builtin_amdgcn_sched_barrier(0);
+      issue_fence();
     }
     if (c < kGmXRing - 1) {
       load_x(c);
-      __builtin_amdgcn_sched_barrier(0);
+      issue_fence();
     }
     if (kGmWRing == 3 && c < kGmWRing) {
       load_w(c, wq[c], wx[c]);
-      __builtin_amdgcn_sched_barrier(0);
+      issue_fence();
     }
   }
 
   const int swz = MX8 ? gemm_swz8(lr) : lr;   // m % 16 == lr for every token tile
-  for (int c0 = 0; c0 < C; c0 += kGmWRing) {
+  // a do-while: C >= 1, and a loop the compiler may skip lets it sink the prologue's weight
+  // loads into the loop's entry block, below the DMA copies
+  int c0 = 0;
+  do {
 #pragma unroll
     for (int sl = 0; sl < kGmWRing; ++sl) {
       const int c = c0 + sl;
@@ -322,7 +329,8 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
       load_w(c + kGmWRing, wq[sl], wx[sl]);   // refill the slot chunk c used, in place
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+    c0 += kGmWRing;
+  } while (c0 < C);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no LDS-DMA write outlives the pass
 
   // epilogue: lane holds rows 4*lg..4*lg+3 of each weight tile for token column lr
