@@ -33,7 +33,10 @@ Readings where the pages are silent (each pinned in tests/test_oracle_pins.py):
   - top-k ties go to the lower expert id; weights = softmax of the k selected logits in double,
     rounded to f32;
   - CSR rows within a bucket are in ascending token order; padding/ghost rows hold -1;
-  - gate_up rows [0, F) are the gate, rows [F, 2F) the up projection.
+  - gate_up rows [0, F) are the gate, rows [F, 2F) the up projection;
+  - the router is a linear layer with bias over bf16 rows ([ext, gpt-oss]), bf16 weights;
+  - MXFP8 activations (the MX-scaled MFMA variant; [ext] OCP 8-bit FP and MX v1.0): an all-zero
+    block takes the smallest scale; elements round to nearest even and saturate at 448.
 
 Every function is pinned (closed forms, invariants, brute force, exact arithmetic); none is
 "parity unpinned".
@@ -187,6 +190,18 @@ def mx8_dequant(codes, scales) -> np.ndarray:
 # --------------------------------------------------------------------------------------------
 # routing and bucketing
 # --------------------------------------------------------------------------------------------
+
+def router_logits(x_bits, w_bits, bias=None) -> np.ndarray:
+    """Router projection: logits[t][e] = bias[e] + sum_d x[t][d] * W_r[e][d], x bf16 [T][D],
+    W_r bf16 [E][D], bias f32 [E] or None; float64 (products of bf16 values are exact, only the
+    sum rounds, at float64). [ext, gpt-oss] the router is a linear layer with bias; the pages
+    start the chain from its output (the per-token expert ids). Also returns S = |bias| +
+    sum_d |x[t][d] * W_r[e][d]|, the scale of the fp32 summation error bound."""
+    x = bf16_to_f64(x_bits)
+    W = bf16_to_f64(w_bits)
+    b = np.zeros(W.shape[0]) if bias is None else np.asarray(bias, dtype=np.float64)
+    return b[None, :] + x @ W.T, np.abs(b)[None, :] + np.abs(x) @ np.abs(W).T
+
 
 def route_topk(logits: np.ndarray, k: int):
     """Top-k routing of each token.

@@ -409,3 +409,34 @@ def test_synthetic_inputs_have_the_workload_distributions():
     assert len(tok["dead"]) == 8 and np.all(tok["logits"][:, tok["dead"]] == -30.0)
     # the same seed regenerates the same arrays
     assert np.array_equal(synth.layer_weights(wl)["down"]["q"], W["down"]["q"])
+
+
+# ---------------------------------------------------------------------------------------------
+# router projection
+# ---------------------------------------------------------------------------------------------
+
+def test_router_logits_hand_case():
+    # x = [1, 2], W_r rows [1, 0], [0.5, -1], [3, 3]; bias [0.25, 0, -1]
+    x = synth.round_f32_to_bf16_bits(np.array([[1.0, 2.0]], np.float32))
+    w = synth.round_f32_to_bf16_bits(np.array([[1.0, 0.0], [0.5, -1.0], [3.0, 3.0]], np.float32))
+    logits, S = oracle.router_logits(x, w, np.array([0.25, 0.0, -1.0], np.float32))
+    assert logits.tolist() == [[1.25, -1.5, 8.0]]
+    assert S.tolist() == [[1.25, 2.5, 10.0]]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_router_logits_exact_brute_force(seed):
+    # every product and sum in exact rational arithmetic; catches a transposed operand, a
+    # dropped bias or a wrong row
+    g = np.random.default_rng(seed)
+    T, E, D = 3, 5, 64
+    x = synth.round_f32_to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    w = synth.round_f32_to_bf16_bits(g.standard_normal((E, D)).astype(np.float32))
+    b = g.standard_normal(E).astype(np.float32)
+    logits, _ = oracle.router_logits(x, w, b)
+    for t in range(T):
+        for e in range(E):
+            exact = Fraction(float(b[e])) + sum(bf16_fraction(x[t, d]) * bf16_fraction(w[e, d])
+                                                for d in range(D))
+            assert abs(Fraction(logits[t, e]) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + \
+                Fraction(1, 2 ** 60)
