@@ -4,6 +4,8 @@
  * The chain (gpt-oss routed experts) runs as five stream-ordered calls:
  *
  *   moe_route_topk  logits -> top-k expert ids + routing weights
+ *   moe_router      x -> router logits, ids, weights and the CSR in one launch (the router
+ *                   projection fused with moe_route_topk and moe_bucket)
  *   moe_bucket      ids    -> CSR of routed rows per expert with padded prefix bases
  *   mx4_pack_experts  one-time repack of MXFP4 expert weights into the GPU's chunked layout
  *   mx4_moe_gemv    gate_up / down MXFP4 projection, few rows per expert (decode)
@@ -197,6 +199,35 @@ int mx4_moe_gemv(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const 
 int mx4_moe_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const mx4_experts* w,
                  const int32_t* counts, const int32_t* basep, int tile_m, int64_t mpad_max,
                  int act, float alpha, float limit, void* out, void* stream);
+
+#define MOE_ROUTER_MAX_ROUTED 16384  /* T*k of one moe_router call */
+
+/*
+ * The router projection and the routing front of the chain in one launch: the step before the
+ * routed chain ([ext, gpt-oss]: the router is a linear layer with bias) fused with top-k and
+ * the bucket pass ([chain]: per-token expert ids in slot order; [fusion]: the padded-prefix
+ * bases computed inside the bucket pass, the CSR unchanged).
+ *   logits[t][e] = b_r[e] + sum_d x[t][d] * W_r[e][d]   bf16 products, fp32 accumulation
+ *   ids, w      = moe_route_topk of those fp32 logits (bit for bit the same decisions)
+ *   counts, basep, row_tok, pos = moe_bucket of those ids with tile_m and mpad_max
+ *   x     bf16 [T][D];  w_r bf16 [E][D];  b_r f32 [E] or NULL.
+ *   logits f32 [T][E] out, or NULL (then not written).
+ *   sync  u32 [1] device workspace owned by the caller: zero before the first call; every call
+ *         leaves it zero. The workgroup that finishes last builds the CSR, found by counting
+ *         on this word, so calls that can run concurrently need distinct words.
+ * Cost: the CSR is built by one workgroup, in time proportional to E * T / 64 steps per
+ * wavefront; for large E * T the separate moe_route_topk + moe_bucket (one workgroup per
+ * expert) spread that work wider.
+ * Errors: MOE_EINVAL for NULL pointers (other than b_r, logits), T, D or E < 1, k < 1,
+ *         k > min(E, MOE_MAX_K); MOE_ESHAPE for D % 32 != 0, T*k > MOE_ROUTER_MAX_ROUTED,
+ *         E > MOE_MAX_E, tile_m outside [1, MOE_MAX_TILE_M], mpad_max < moe_mpad_max(T, k, E,
+ *         tile_m), x or W_r of 2 GB or more; MOE_EALIGN for x or w_r not 16-byte aligned;
+ *         MOE_ELAUNCH.
+ */
+int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b_r, int64_t T, int D,
+               int E, int k, int tile_m, int64_t mpad_max, float* logits, int32_t* ids, float* w,
+               int32_t* counts, int32_t* basep, int32_t* row_tok, int32_t* pos, uint32_t* sync,
+               void* stream);
 
 /*
  * MXFP8 activations: the projections on the MX-scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4,

@@ -19,7 +19,8 @@ MOE_MAX_K, MOE_MAX_E, MOE_MAX_TILE_M = 16, 1024, 256
 
 EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_pack_experts",
            "mx4_moe_gemv", "mx4_moe_gemm", "moe_combine", "mx4_moe_decode", "moe_timing_arm",
-           "moe_timing_read", "mx8_quantize", "mx4_moe_gemm_mx8")
+           "moe_timing_read", "mx8_quantize", "mx4_moe_gemm_mx8", "moe_router")
+MOE_ROUTER_MAX_ROUTED = 16384
 MOE_MX8_GEMM_MAX_K = 8192
 
 
@@ -70,6 +71,9 @@ def lib() -> ctypes.CDLL:
         L.mx4_moe_decode.restype = ci
         L.mx4_moe_decode.argtypes = [vp, vp, i64, ci, ci, pe, pe, cf, cf,
                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_router.restype = ci
+        L.moe_router.argtypes = [vp, vp, vp, i64, ci, ci, ci, ci, i64, vp, vp, vp, vp, vp, vp,
+                                 vp, vp, vp]
         L.mx8_quantize.restype = ci
         L.mx8_quantize.argtypes = [vp, vp, i64, ci, vp, vp, vp]
         L.mx4_moe_gemm_mx8.restype = ci
@@ -198,6 +202,37 @@ def moe_route_topk(logits, k: int, ids=None, w=None, stream=None):
     w = torch.empty((T, k), dtype=torch.float32, device=logits.device) if w is None else w
     _call("moe_route_topk", _ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(stream))
     return ids, w
+
+
+def moe_router(x, w_r, b_r, k: int, tile_m: int, sync, mpad_max: int | None = None,
+               want_logits: bool = True, out=None, stream=None):
+    """Router projection + top-k + bucket in one launch. x bf16 [T][D], w_r bf16 [E][D], b_r f32
+    [E] or None, sync a zeroed int32/uint32 device tensor of one element (left zero). Returns a
+    dict: logits (if want_logits), ids, w, counts, basep, row_tok, pos, mpad."""
+    torch = _torch()
+    _check(x, torch.bfloat16, "x")
+    _check(w_r, torch.bfloat16, "w_r")
+    if b_r is not None:
+        _check(b_r, torch.float32, "b_r")
+    T, D = x.shape
+    E = w_r.shape[0]
+    if mpad_max is None:
+        mpad_max = moe_mpad_max(T, k, E, tile_m)
+    dev = x.device
+    o = dict(out or {})
+    shapes = {"ids": ((T, k), torch.int32), "w": ((T, k), torch.float32),
+              "counts": ((E,), torch.int32), "basep": ((E + 1,), torch.int32),
+              "row_tok": ((mpad_max,), torch.int32), "pos": ((T, k), torch.int32)}
+    if want_logits:
+        shapes["logits"] = ((T, E), torch.float32)
+    for key, (shape, dt) in shapes.items():
+        if key not in o:
+            o[key] = torch.empty(shape, dtype=dt, device=dev)
+    _call("moe_router", _ptr(x), _ptr(w_r), _ptr(b_r), T, D, E, k, tile_m, mpad_max,
+          _ptr(o.get("logits")), _ptr(o["ids"]), _ptr(o["w"]), _ptr(o["counts"]), _ptr(o["basep"]),
+          _ptr(o["row_tok"]), _ptr(o["pos"]), _ptr(sync), _stream(stream))
+    o["mpad"] = mpad_max
+    return o
 
 
 def moe_bucket(ids, E: int, tile_m: int, mpad_max: int | None = None, out=None, stream=None):

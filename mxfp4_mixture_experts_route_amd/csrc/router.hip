@@ -1,0 +1,218 @@
+// moe_router: the router projection and the routing front of the chain in one launch:
+// logits = x W_r^T + b_r (bf16 MFMA, fp32 accumulation), top-k + softmax weights per token, and
+// the bucket/CSR with padded prefix bases over all tokens.
+//
+// Sources: PR #3579 "dasLLAMA gpt-oss arc" (fused MoE expert chain commit: per-token expert ids
+// in slot order; Metal fusion-lane commit: the bucket pass computes the padded-prefix bases
+// itself instead of a separate prefix pass, the CSR unchanged bit for bit). The router itself is
+// the gpt-oss linear layer with bias [ext]; the pages start from its output.
+//
+// gfx950 mapping. Workgroups of 16 wavefronts each take 16 tokens:
+//  * logits: v_mfma_f32_16x16x32_bf16 with 16 router rows (experts) as the A operand and the 16
+//    tokens as the B columns; the K = D reduction is split over the wavefronts that share an
+//    expert tile (16 / ceil(E/16) of them), whose partial tiles meet in LDS and are summed in a
+//    fixed order, then the bias is added. Loads are buffer loads: tokens past T and experts past
+//    E read zeros.
+//  * top-k: one wavefront per token on the LDS logits row (the moe_route_topk code).
+//  * bucket: the CSR needs every token's ids, so the LAST workgroup to finish its tokens builds
+//    it: each workgroup publishes its ids (device-scope release fence) and increments a
+//    caller-provided counter; the one that brings it to the grid size acquires, copies all ids
+//    into LDS, histograms them, scans the padded counts into basep, and compacts each expert's
+//    rows in ascending token order (each wavefront owns whole experts, one ballot per 64
+//    tokens), then resets the counter to zero. No workgroup ever waits for another.
+#include "route_core.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kRtWaves = 16;
+constexpr int kRtThreads = kRtWaves * kWave;
+constexpr int kRtTok = 16;   // tokens per workgroup
+
+// expert tiles and the K split of the logits stage
+__host__ __device__ inline int rt_tiles(int E) { return (E + 15) / 16; }
+__host__ __device__ inline int rt_ksplit(int E) {
+  const int n = rt_tiles(E);
+  return n >= kRtWaves ? 1 : kRtWaves / n;
+}
+// dynamic LDS: the logits stage's partial tiles, or the bucket's histogram, bases and ids
+__host__ inline size_t rt_lds_bytes(int E, int64_t R) {
+  const size_t p1 = (size_t)rt_ksplit(E) * kRtTok * E * sizeof(float);
+  const size_t p2 = (size_t)(2 * E + R) * sizeof(int);
+  return p1 > p2 ? p1 : p2;
+}
+
+__global__ void __launch_bounds__(kRtThreads)
+router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+              const float* __restrict__ br, int T, int D, int E, int k, int tile_m,
+              int mpad_max, float* __restrict__ logits, int32_t* __restrict__ ids,
+              float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ basep,
+              int32_t* __restrict__ row_tok, int32_t* __restrict__ pos,
+              uint32_t* __restrict__ sync) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_last;
+  __shared__ int s_wave_tot[kRtWaves];
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int t0 = (int)blockIdx.x * kRtTok;
+  const int ntiles = rt_tiles(E), ksplit = rt_ksplit(E);
+  const int KS = D >> 5;   // 32-wide k steps
+  float* part = reinterpret_cast<float*>(smem);   // [ksplit][kRtTok][E]
+
+  // ---- logits of the workgroup's 16 tokens ----
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wr, (uint32_t)E * D * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)T * D * 2);
+  for (int u = wave; u < ntiles * ksplit; u += kRtWaves) {
+    const int tile = u % ntiles, p = u / ntiles;
+    const int s0 = p * KS / ksplit, s1 = (p + 1) * KS / ksplit;
+    const int e_row = tile * 16 + lr;
+    const uint32_t ao = e_row < E ? ((uint32_t)e_row * D + 8 * lg) * 2 : kOOB;
+    const uint32_t bo = t0 + lr < T ? ((uint32_t)(t0 + lr) * D + 8 * lg) * 2 : kOOB;
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    int s = s0;
+    for (; s + 1 < s1; s += 2) {   // two independent chains
+      const u32x4_t a0 = buf_load16(rw, ao, (uint32_t)s * 64), b0 = buf_load16(rx, bo, (uint32_t)s * 64);
+      const u32x4_t a1 = buf_load16(rw, ao, (uint32_t)s * 64 + 64);
+      const u32x4_t b1 = buf_load16(rx, bo, (uint32_t)s * 64 + 64);
+      bf16x8_t A0, B0, A1, B1;
+      __builtin_memcpy(&A0, &a0, 16);
+      __builtin_memcpy(&B0, &b0, 16);
+      __builtin_memcpy(&A1, &a1, 16);
+      __builtin_memcpy(&B1, &b1, 16);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B1, acc1, 0, 0, 0);
+    }
+    if (s < s1) {
+      const u32x4_t a0 = buf_load16(rw, ao, (uint32_t)s * 64), b0 = buf_load16(rx, bo, (uint32_t)s * 64);
+      bf16x8_t A0, B0;
+      __builtin_memcpy(&A0, &a0, 16);
+      __builtin_memcpy(&B0, &b0, 16);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, acc0, 0, 0, 0);
+    }
+    // lane holds experts tile*16 + 4*lg + i of token lr
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tile * 16 + 4 * lg + i;
+      if (e < E) part[((size_t)p * kRtTok + lr) * E + e] = acc0[i] + acc1[i];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kRtTok * E; i += kRtThreads) {
+    const int tok = i / E, e = i - tok * E;
+    float v = part[(size_t)tok * E + e];
+    for (int p = 1; p < ksplit; ++p) v += part[((size_t)p * kRtTok + tok) * E + e];
+    if (br) v += br[e];
+    part[(size_t)tok * E + e] = v;   // only this thread touches element (tok, e)
+    if (logits && t0 + tok < T) logits[(size_t)(t0 + tok) * E + e] = v;
+  }
+  __syncthreads();
+
+  // ---- top-k: wavefront w routes token t0 + w ----
+  if (t0 + wave < T) {
+    int my_id;
+    float my_v;
+    wave_topk(part + (size_t)wave * E, E, k, my_id, my_v);
+    write_topk(my_id, my_v, k, ids + (size_t)(t0 + wave) * k, w + (size_t)(t0 + wave) * k);
+  }
+
+  // ---- the last workgroup builds the CSR ----
+  __threadfence();   // release: this workgroup's ids before its count
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(sync, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();   // acquire: every workgroup's ids
+
+  const int R = T * k;
+  int* hist = reinterpret_cast<int*>(smem);
+  int* base = hist + E;
+  int* idl = base + E;
+  for (int i = tid; i < E; i += kRtThreads) hist[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < R; i += kRtThreads) {
+    const int id = ids[i];
+    idl[i] = id;
+    if ((unsigned)id < (unsigned)E) atomicAdd(&hist[id], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the padded counts over the experts (E <= 1024: one per thread)
+  const int cnt = tid < E ? hist[tid] : 0;
+  const int padded = (cnt + tile_m - 1) / tile_m * tile_m;
+  int incl = padded;
+  for (int m = 1; m < 64; m <<= 1) {
+    const int o = __shfl_up(incl, m);
+    if (lane >= m) incl += o;
+  }
+  if (lane == 63) s_wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int v = 0; v < kRtWaves; ++v) {
+    if (v < wave) before += s_wave_tot[v];
+    total += s_wave_tot[v];
+  }
+  const int excl = before + incl - padded;
+  if (tid < E) {
+    base[tid] = excl;
+    counts[tid] = cnt;
+    basep[tid] = excl;
+  }
+  if (tid == 0) basep[E] = total;
+  __syncthreads();
+  // ordered compaction: wavefront v owns experts v, v + 16, ...
+  for (int e = wave; e < E; e += kRtWaves) {
+    const int b = base[e];
+    int running = 0;
+    for (int tt = 0; tt < T; tt += 64) {
+      const int t = tt + lane;
+      int slot = -1;
+      if (t < T)
+        for (int s = 0; s < k; ++s)
+          if (idl[t * k + s] == e) slot = s;
+      const uint64_t ballot = __ballot(slot >= 0);
+      if (slot >= 0) {
+        const int r = b + running + __popcll(ballot & (lane ? (~0ull >> (64 - lane)) : 0ull));
+        row_tok[r] = t;
+        pos[(size_t)t * k + slot] = r;
+      }
+      running += __popcll(ballot);
+    }
+    const int pe = (running + tile_m - 1) / tile_m * tile_m;
+    for (int r = b + running + lane; r < b + pe; r += 64) row_tok[r] = -1;   // padding rows
+  }
+  for (int r = total + tid; r < mpad_max; r += kRtThreads) row_tok[r] = -1;   // ghost rows
+  if (tid == 0) atomicExch(sync, 0u);   // ready for the next call
+}
+
+}  // namespace moe
+
+extern "C" int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b_r, int64_t T,
+                          int D, int E, int k, int tile_m, int64_t mpad_max, float* logits,
+                          int32_t* ids, float* w, int32_t* counts, int32_t* basep,
+                          int32_t* row_tok, int32_t* pos, uint32_t* sync, void* stream) {
+  if (!x || !w_r || !ids || !w || !counts || !basep || !row_tok || !pos || !sync || T < 1 ||
+      D < 1 || E < 1 || k < 1 || k > E || k > MOE_MAX_K)
+    return MOE_EINVAL;
+  if (E > MOE_MAX_E || D % 32 != 0 || T * k > MOE_ROUTER_MAX_ROUTED || tile_m < 1 ||
+      tile_m > MOE_MAX_TILE_M || T * (int64_t)D * 2 >= (1LL << 31) ||
+      (int64_t)E * D * 2 >= (1LL << 31))
+    return MOE_ESHAPE;
+  const int64_t need = moe_mpad_max(T, k, E, tile_m);
+  if (mpad_max < need || mpad_max > 0x7FFFFFFFLL) return MOE_ESHAPE;
+  if ((((uintptr_t)x) & 15) || (((uintptr_t)w_r) & 15)) return MOE_EALIGN;
+  const size_t lds = moe::rt_lds_bytes(E, T * k);
+  static bool lds_attr_set = false;
+  if (!lds_attr_set) {
+    const size_t most = moe::rt_lds_bytes(MOE_MAX_E, MOE_ROUTER_MAX_ROUTED);
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::router_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)most) != hipSuccess)
+      return MOE_ELAUNCH;
+    lds_attr_set = true;
+  }
+  const int64_t blocks = (T + moe::kRtTok - 1) / moe::kRtTok;
+  moe::launch(moe::router_kernel, dim3((unsigned)blocks), dim3(moe::kRtThreads), (unsigned)lds,
+              (hipStream_t)stream, x, w_r, b_r, (int)T, D, E, k, tile_m, (int)mpad_max, logits,
+              ids, w, counts, basep, row_tok, pos, sync);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}

@@ -209,3 +209,27 @@ def test_gemm_mx8_argument_checks():
     assert call(aq=ctypes.c_void_p(0x1008)) == _lib.MOE_EALIGN
     assert call(as_=ctypes.c_void_p(0x1008)) == _lib.MOE_EALIGN
     assert call(out=ctypes.c_void_p(0x1002)) == _lib.MOE_EALIGN
+
+
+@no_gpu
+def test_router_argument_checks():
+    f = _lib.lib().moe_router
+
+    def call(x=FAKE, w_r=FAKE, b_r=None, T=4, D=64, E=8, k=2, tile_m=4, mpad=64, logits=None,
+             sync=FAKE):
+        return f(x, w_r, b_r, T, D, E, k, tile_m, mpad, logits, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 FAKE, sync, None)
+
+    assert call(x=None) == _lib.MOE_EINVAL
+    assert call(w_r=None) == _lib.MOE_EINVAL
+    assert call(sync=None) == _lib.MOE_EINVAL
+    assert call(T=0) == _lib.MOE_EINVAL
+    assert call(k=9) == _lib.MOE_EINVAL
+    assert call(k=17, E=32) == _lib.MOE_EINVAL
+    assert call(D=48) == _lib.MOE_ESHAPE
+    assert call(E=2048, k=2) == _lib.MOE_ESHAPE
+    assert call(T=5000, k=4, mpad=1 << 20) == _lib.MOE_ESHAPE     # T*k > MOE_ROUTER_MAX_ROUTED
+    assert call(tile_m=0) == _lib.MOE_ESHAPE
+    assert call(mpad=7) == _lib.MOE_ESHAPE
+    assert call(x=ctypes.c_void_p(0x1008)) == _lib.MOE_EALIGN
+    assert call(w_r=ctypes.c_void_p(0x1004)) == _lib.MOE_EALIGN
