@@ -7,7 +7,8 @@ dim = ffn = 2880, top-4, one token, through 24 distinct seeded MoE layers (10.15
 experts resident in HBM, 1.27 GB touched per step, far more than the 256 MB last-level cache), so a
 step is one decode token through the model's 24 MoE layers, replayed as one HIP graph. Each layer
 runs as mx4_moe_decode (the chain fused into two launches); the five-call chain (route, bucket,
-GEMV, GEMV, combine) is timed beside it.
+GEMV, GEMV, combine) is timed beside it, and moe_router (router projection + top-k + CSR in one
+launch) on the same tokens.
 
 Prints ONE JSON line. `value` = decode tokens/s through the 24-layer stack. The same line also
 carries the dominant kernel's roofline, the decode weight GB/s of the two MXFP4 projections, the
@@ -200,6 +201,22 @@ def kernel_times_us(moe, torch, layers, call, launches, reps, sleep_cycles):
     return [1000.0 * v / n for v in sums]
 
 
+def router_us(moe, torch, layers, wl, reps, sleep_cycles):
+    """Kernel time of moe_router (router projection + top-k + CSR, one launch) on the layers'
+    x with a seeded bf16 router [E][D] and bias, writing into the layers' routing buffers."""
+    g = torch.Generator(device="cpu").manual_seed(99)
+    wr = (torch.randn((wl.E, wl.dim), generator=g) / wl.dim ** 0.5).to(torch.bfloat16).cuda()
+    br = (torch.randn(wl.E, generator=g) * 0.1).cuda()
+    sync = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def call(L):
+        c = L.csr
+        moe.moe_router(L.x, wr, br, wl.k, wl.tile_m, sync, mpad_max=L.mpad, want_logits=False,
+                       out={"ids": L.ids, "w": L.w, "counts": c[0], "basep": c[1],
+                            "row_tok": c[2], "pos": c[3]})
+    return kernel_times_us(moe, torch, layers, call, 1, reps, sleep_cycles)[0]
+
+
 def touched_experts(torch, layers):
     return [int(torch.unique(L.ids).numel()) for L in layers]
 
@@ -310,6 +327,7 @@ def main():
     chain_us = kernel_times_us(moe, torch, layers, lambda L: L.chain(), 5, args.kernel_reps,
                                sleep_cycles)
     n_touch = touched_experts(torch, layers)
+    decode_router_us = router_us(moe, torch, layers, wl, args.kernel_reps, sleep_cycles)
     per_expert_gu = 2 * wl.ffn * wl.dim * 17 // 32          # nibbles + scales, bytes
     per_expert_dn = wl.dim * wl.ffn * 17 // 32
     avg_touch = sum(n_touch) / len(n_touch)
@@ -354,7 +372,8 @@ def main():
                                        "gemv_down_us": round(chain_us[3], 3),
                                        "combine_us": round(chain_us[4], 3),
                                        "gemv_weight_GBps": round(gemv_gbps, 1)},
-                   "touched_experts_per_layer": avg_touch},
+                   "touched_experts_per_layer": avg_touch,
+                   "router_us": round(decode_router_us, 3)},
     }
     del layers
     torch.cuda.empty_cache()
@@ -398,6 +417,8 @@ def main():
             "chain_tokens_per_s": round(pw.T * pw.layers * p_steps / msecs, 1),
             "per_layer_chain_us": round(1e6 * msecs / (p_steps * pw.layers), 2),
         }
+        result["prefill_pp512"]["router_us"] = round(
+            router_us(moe, torch, players, pw, args.kernel_reps, sleep_cycles), 2)
         del players
         torch.cuda.empty_cache()
 

@@ -265,7 +265,7 @@ int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b_r, int64_t
  * Errors: as mx4_moe_gemm (aq in place of a, also NULL as), plus MOE_ESHAPE for
  *         K > MOE_MX8_GEMM_MAX_K and MOE_EALIGN for as not 16-byte aligned.
  */
-#define MOE_MX8_GEMM_MAX_K 8192  /* reduction length of mx4_moe_gemm_mx8 (LDS scale staging) */
+#define MOE_MX8_GEMM_MAX_K 4096  /* reduction length of mx4_moe_gemm_mx8 (LDS scale staging) */
 
 int mx8_quantize(const uint16_t* a, const int32_t* live, int64_t rows, int K, uint8_t* q,
                  uint8_t* s, void* stream);

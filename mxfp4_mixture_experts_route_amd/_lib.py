@@ -21,7 +21,7 @@ EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_
            "mx4_moe_gemv", "mx4_moe_gemm", "moe_combine", "mx4_moe_decode", "moe_timing_arm",
            "moe_timing_read", "mx8_quantize", "mx4_moe_gemm_mx8", "moe_router")
 MOE_ROUTER_MAX_ROUTED = 16384
-MOE_MX8_GEMM_MAX_K = 8192
+MOE_MX8_GEMM_MAX_K = 4096
 
 
 class MoeError(RuntimeError):

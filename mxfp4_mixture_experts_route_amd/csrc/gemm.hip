@@ -58,8 +58,9 @@
 namespace moe {
 
 constexpr int kGmWaves = 8;              // 2 wavefronts per SIMD
+constexpr int kXcds = 8;                 // XCDs of an MI355X, each with its own L2
 constexpr int kGmThreads = 64 * kGmWaves;
-constexpr int kGmMaxWT = 3;              // weight tiles (16 rows each) per wavefront, at most
+constexpr int kGmMaxWT = 6;              // weight tiles (16 rows each) per wavefront, at most
 // SwiGLU: 2 tiles (16 gate rows + the matching 16 up rows); plain: 3 tiles (384 rows per
 // workgroup), which at gpt-oss shapes makes the down projection's grid a whole number of
 // rounds over the 256 CUs (2880 / 384 -> 8 workgroups per expert)
@@ -80,8 +81,11 @@ __host__ __device__ constexpr int gemm_buf_bytes(int ntt, bool mx8) {
 }
 // after the activation ring: 1 KB that the DMA of wavefronts without a share of a chunk writes;
 // MXFP8 passes then stage the e8m0 scale rows of their 128 routed rows
+// MXFP8 passes hold two super-chunks of activations (a super-chunk = one weight ring's worth of
+// chunks, at most 4) instead of a ring of 4 chunks: the same 128 KB
+constexpr int kGmScMax = 4;
 __host__ __device__ constexpr int gemm_dummy_off(bool mx8) {
-  return kGmXRing * gemm_buf_bytes(kGmTT, mx8);
+  return (mx8 ? 2 * kGmScMax : kGmXRing) * gemm_buf_bytes(kGmTT, mx8);
 }
 // LDS pitch of a staged scale row: fixed, so that a token tile's offset is an immediate
 constexpr int kGmScalePitch = MOE_MX8_GEMM_MAX_K / 32;
@@ -106,18 +110,63 @@ struct GemmCtx {
   int tile_base[kGmMaxWT];
   int rows_in[kGmMaxWT];
   uint32_t wo[kGmMaxWT], wol[kGmMaxWT], so[kGmMaxWT];
+  uint32_t sg[kGmMaxWT];   // the lane's scale row (16-byte groups of 4 chunks)
 };
 
-// One pass with NTT live token tiles (compile-time, so the MFMA loop is straight-line code and
-// LDS reads can be scheduled ahead of the MFMAs that use them). MX8: MXFP8 activations on the
-// MX-scaled MFMA, else bf16 activations on bf16 MFMA.
-template <int ACT, int NTT, bool MX8>
+// Epilogue of a pass: lane holds rows 4*lg..4*lg+3 of each weight tile for token column lr.
+// SwiGLU: tiles [0, WT/2) are gate rows, tile t + WT/2 the matching up rows.
+template <int ACT, int NTT, int WT>
+__device__ __forceinline__ void gemm_epilogue(const GemmCtx& g, const f32x4_t (&acc)[WT][NTT]) {
+  constexpr bool swiglu = (ACT == MOE_ACT_SWIGLU_OAI);
+  constexpr int kGmWT = WT;
+  const int lr = g.lr, lg = g.lg;
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    const int m = tt * 16 + lr;
+    if (m >= g.live) continue;
+    const size_t r = (size_t)(g.row0 + g.p0 + m);
+    if (swiglu) {
+#pragma unroll
+      for (int t = 0; t < WT / 2; ++t) {
+        const int j0 = g.tile_base[t] + 4 * lg;
+        uint16_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          h[i] = (uint16_t)f32_to_bf16_bits(
+              swiglu_oai(acc[t][tt][i], acc[t + WT / 2][tt][i], g.alpha, g.limit));
+        uint16_t* dst = reinterpret_cast<uint16_t*>(g.out) + r * g.F + j0;
+        if (4 * lg + 4 <= g.rows_in[t] && (g.F & 3) == 0) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                      (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if (4 * lg + i < g.rows_in[t]) dst[i] = h[i];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < kGmWT; ++t) {
+        float* dst = reinterpret_cast<float*>(g.out) + r * g.N + g.tile_base[t] + 4 * lg;
+        if (4 * lg + 4 <= g.rows_in[t] && (g.N & 3) == 0) {
+          *reinterpret_cast<f32x4_t*>(dst) = acc[t][tt];
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if (4 * lg + i < g.rows_in[t]) dst[i] = acc[t][tt][i];
+        }
+      }
+    }
+  }
+}
+
+// One pass with NTT live token tiles over bf16 activations, on bf16 MFMA (compile-time NTT, so
+// the MFMA loop is straight-line code and LDS reads can be scheduled ahead of the MFMAs).
+template <int ACT, int NTT>
 __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict__ xs) {
   constexpr bool swiglu = (ACT == MOE_ACT_SWIGLU_OAI);
   constexpr int kGmWT = gemm_wt(ACT);
-  constexpr int ROWB = gemm_row_bytes(MX8);
+  constexpr int ROWB = gemm_row_bytes(false);
   constexpr int PIECES = ROWB / 16;          // 16-byte pieces per row per chunk
-  constexpr int BUF = gemm_buf_bytes(NTT, MX8);
+  constexpr int BUF = gemm_buf_bytes(NTT, false);
   constexpr int KBS = BUF / 1024;            // 1 KB DMA instructions per chunk
   // DMA instructions per wavefront per chunk: the chunk's KBS KB split over the wavefronts,
   // every wavefront issuing the same count (surplus ones copy zeros into a dummy KB) so that
@@ -129,7 +178,7 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
   const int lr = g.lr, lg = g.lg;
   const int lane = g.tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(g.tid >> 6);   // uniform: LDS-DMA base
-  const int dummy = gemm_dummy_off(MX8);
+  const int dummy = gemm_dummy_off(false);
 
   // weight fetch of chunk c into a ring slot. Chunks past K re-read the last chunk (their
   // compute is skipped), so every chunk issues the same loads and only the last one differs
@@ -147,24 +196,23 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
   };
 
   // activation DMA: instruction i of this wavefront covers 16-byte slots p = j*64 + lane,
-  // j = wave + 8*i, i.e. routed row m = p / PIECES of the pass and swizzled slot p % PIECES,
-  // which holds the row's piece q = (p % PIECES) ^ swz(m) of the chunk (bf16: swz = m % 16;
-  // MXFP8: gemm_swz8)
+  // j = wave + 8*i, i.e. routed row m = p / 16 of the pass and swizzled slot p % 16, which
+  // holds the row's piece q = (p % 16) ^ (m % 16) of the chunk
   uint32_t xo[NX], xol[NX];
 #pragma unroll
   for (int i = 0; i < NX; ++i) {
     const int p = (wave + kGmWaves * i) * 64 + lane;
     const int m = p / PIECES;
-    const int q = (p % PIECES) ^ (MX8 ? gemm_swz8(m) : (m & 15));
+    const int q = (p % PIECES) ^ (m & 15);
     uint32_t off = kOOB;
     if (m < g.live && wave + kGmWaves * i < KBS) {
       const int r = g.row0 + g.p0 + m;
       const uint32_t src = g.a_row ? (uint32_t)g.a_row[r] : (uint32_t)r;
-      off = src * (uint32_t)g.K * (MX8 ? 1u : 2u) + q * 16;
+      off = src * (uint32_t)g.K * 2 + q * 16;
     }
     xo[i] = off;
     // the last chunk may be narrower than 128 k
-    xol[i] = (q * 16 < g.klast * (MX8 ? 1 : 2)) ? off : kOOB;
+    xol[i] = (q * 8 < g.klast) ? off : kOOB;
   }
   auto load_x = [&](int c) {
     const int cc = min(c, C - 1);
@@ -199,26 +247,6 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
   uint32_t wx[kGmWRing][kGmWT];
 
   __syncthreads();  // the previous pass is done with the LDS buffers
-  // MXFP8: the e8m0 scale rows of the pass's routed rows, row m at xsc + m * kGmScalePitch
-  // (the bytes past the row's spa read as zeros), by LDS-DMA ahead of everything else: one
-  // instruction per 4 rows. The first wait of the K loop covers them (loads complete in issue
-  // order).
-  uint8_t* const xsc = xs + dummy + 1024;
-  if (MX8) {
-    constexpr int kRowsPerKB = 1024 / kGmScalePitch;
-    for (int j = wave; j < NTT * 16 / kRowsPerKB; j += kGmWaves) {
-      const int m = j * kRowsPerKB + lane / (kGmScalePitch / 16);
-      const int piece = lane % (kGmScalePitch / 16);
-      uint32_t off = kOOB;
-      if (m < g.live && piece * 16 < g.spa) {
-        const int r = g.row0 + g.p0 + m;
-        const uint32_t src = g.a_row ? (uint32_t)g.a_row[r] : (uint32_t)r;
-        off = src * (uint32_t)g.spa + piece * 16;
-      }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          g.ras, (__attribute__((address_space(3))) void*)(xsc + j * 1024), 16, off, 0, 0, 0);
-    }
-  }
   // prologue, in the steady state's issue order (W0 X0 W1 X1 W2 X2 W3 with a ring of 4;
   // X0 W0 X1 W1 X2 W2 with a ring of 3)
   // (issue_fence, not only a scheduling barrier: the plain weight loads would otherwise sink
@@ -241,7 +269,7 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
     }
   }
 
-  const int swz = MX8 ? gemm_swz8(lr) : lr;   // m % 16 == lr for every token tile
+  const int swz = lr;   // m % 16 == lr for every token tile
   // a do-while: C >= 1, and a loop the compiler may skip lets it sink the prologue's weight
   // loads into the loop's entry block, below the DMA copies
   int c0 = 0;
@@ -264,22 +292,203 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
       __builtin_amdgcn_sched_barrier(0);
       if (c < C) {
         const uint8_t* xb = xs + (c % kGmXRing) * BUF;
-        if constexpr (MX8) {
-          // v_mfma_scale_f32_16x16x128_f8f6f4: A = the lane's 16-byte MX block as 32 e2m1
-          // values (weight row lr, block 4c + lg) with its e8m0 byte as scale; B = 32 E4M3
-          // values of token column lr: k 16*lg..16*lg+15 and 64+16*lg..64+16*lg+15 of the
-          // chunk, with the scale of block 4c + lg. Blocks past K take scale 0 (their data
-          // are zeros) so that no padding byte can inject a NaN scale.
-          const bool kb_live = 4 * c + lg < g.KB;
-          int sa[kGmWT];
+        float cs[kGmWT];
 #pragma unroll
-          for (int t = 0; t < kGmWT; ++t) sa[t] = kb_live ? (int)wx[sl][t] : 0;
-          // B fragments of token tile tt + 1 are read from LDS while tile tt's MFMAs run (one
-          // tile ahead, not all of them: 8 tiles of 9 VGPRs would not fit beside the ring)
-          // per-lane bases; a token tile adds a constant (an instruction offset)
+        for (int t = 0; t < kGmWT; ++t) cs[t] = e8m0_scale_operand(wx[sl][t]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x8_t A[kGmWT];
+#pragma unroll
+          for (int t = 0; t < kGmWT; ++t) A[t] = dequant8(wq[sl][t][i], cs[t]);
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt) {
+            const int m = tt * 16 + lr;   // m % 16 == lr
+            const bf16x8_t B =
+                *reinterpret_cast<const bf16x8_t*>(xb + (m * 16 + ((lg * 4 + i) ^ swz)) * 16);
+#pragma unroll
+            for (int t = 0; t < kGmWT; ++t)
+              acc[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t], B, acc[t][tt], 0, 0, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(c + kGmWRing, wq[sl], wx[sl]);   // refill the slot chunk c used, in place
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    c0 += kGmWRing;
+  } while (c0 < C);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no LDS-DMA write outlives the pass
+
+  gemm_epilogue<ACT, NTT, kGmWT>(g, acc);
+}
+
+// MXFP8 pass on the MX-scaled MFMA. The arithmetic per byte is small here (no decode, one MFMA
+// per 16x16x128 tile product), so the pass is bound by how many weight bytes are in flight: one
+// wavefront per SIMD (4 per workgroup) with its accumulators allowed into the AGPR half of the
+// register file, so each wavefront can hold a deep ring of weight chunks (SwiGLU: 8 chunks of 4
+// tiles, 32 KB; plain: 4 chunks of 6 tiles, 24 KB). The activations move in super-chunks of 4
+// chunks, double-buffered in LDS, so the workgroup meets at a barrier once per 4 chunks; between
+// barriers each wavefront streams its own weights.
+//  * Issue order per super-chunk: the DMA of the next super-chunk, then after each chunk's MFMAs
+//    the weight chunk WRING ahead into the slot just used. At the top of super-chunk s, waiting
+//    until only the 4 weight chunks issued after its DMA are outstanding lands that DMA (loads
+//    complete in issue order); the barrier makes it every wavefront's and frees the half that
+//    the next DMA overwrites. The weights of each chunk are waited for by the compiler
+//    (register dependencies).
+constexpr int kMxWaves = 4;
+constexpr int kMxThreads = 64 * kMxWaves;
+constexpr int kMxSC = 4;   // chunks per activation super-chunk
+__host__ __device__ constexpr int mx_wt(int act) { return act == MOE_ACT_SWIGLU_OAI ? 4 : 6; }
+__host__ __device__ constexpr int mx_wring(int act) { return act == MOE_ACT_SWIGLU_OAI ? 8 : 4; }
+constexpr int SRING_MAX = 2;   // scale groups in flight, at most (mx_wring / kMxSC)
+static_assert(gemm_dummy_off(true) == 2 * kMxSC * gemm_buf_bytes(kGmTT, true), "MX LDS layout");
+
+template <int ACT, int NTT>
+__device__ __forceinline__ void gemm_pass_mx8(const GemmCtx& g, uint8_t* __restrict__ xs) {
+  constexpr int WT = mx_wt(ACT);
+  constexpr int WRING = mx_wring(ACT);
+  constexpr int SC = kMxSC;
+  constexpr int ITER = WRING > SC ? WRING : SC;   // chunks per loop trip (slots compile-time)
+  static_assert(ITER % SC == 0 && ITER % WRING == 0, "loop trip");
+  constexpr int ROWB = gemm_row_bytes(true);      // 128 E4M3 bytes per row per chunk
+  constexpr int PIECES = ROWB / 16;
+  constexpr int BUF = gemm_buf_bytes(NTT, true);
+  constexpr int KBS = BUF / 1024;                 // 1 KB DMA instructions per chunk
+  constexpr int NX = (KBS + kMxWaves - 1) / kMxWaves;
+  static_assert(WT * (WRING + SRING_MAX) + 4 * SC <= 63, "loads in flight per wavefront");
+  const int C = g.C;
+  const int lr = g.lr, lg = g.lg;
+  const int lane = g.tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(g.tid >> 6);
+  const int dummy = gemm_dummy_off(true);
+
+  // nibbles of chunk c into a ring slot (chunks past K re-read the last one)
+  auto load_w = [&](int c, u32x4_t (&dq)[WT]) {
+    const int cc = min(c, C - 1);
+    const bool last = cc == C - 1;
+    const uint32_t cq = (uint32_t)cc * g.N * (kChunkBlocks * 16);
+#pragma unroll
+    for (int t = 0; t < WT; ++t) dq[t] = buf_load16(g.rq, last ? g.wol[t] : g.wo[t], cq);
+  };
+  // e8m0 scales of the SC chunks of super-chunk s, one 16-byte load per tile: the scale of
+  // chunk s*SC + j for this lane is byte lg of dword j (super-chunks past K re-read the last)
+  static_assert(SC == 4, "a 16-byte scale load covers 4 chunks");
+  const int S_last = (C - 1) / SC;
+  auto load_s = [&](int s, u32x4_t (&ds)[WT]) {
+    const uint32_t off = (uint32_t)min(s, S_last) * 16;
+#pragma unroll
+    for (int t = 0; t < WT; ++t) ds[t] = buf_load16(g.rs, g.sg[t], off);
+  };
+
+  // activation DMA slots of this wavefront: 16-byte slot p = (wave + 4*i)*64 + lane of a chunk
+  // buffer holds piece (p % 8) ^ gemm_swz8(m) of routed row m = p / 8
+  uint32_t xo[NX], xol[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int p = (wave + kMxWaves * i) * 64 + lane;
+    const int m = p / PIECES;
+    const int q = (p % PIECES) ^ gemm_swz8(m);
+    uint32_t off = kOOB;
+    if (m < g.live && wave + kMxWaves * i < KBS) {
+      const int r = g.row0 + g.p0 + m;
+      const uint32_t src = g.a_row ? (uint32_t)g.a_row[r] : (uint32_t)r;
+      off = src * (uint32_t)g.K + q * 16;
+    }
+    xo[i] = off;
+    xol[i] = (q * 16 < g.klast) ? off : kOOB;
+  }
+  // super-chunk s into LDS half s % 2 (chunks past K re-read the last one)
+  auto load_x_super = [&](int s) {
+#pragma unroll
+    for (int j = 0; j < SC; ++j) {
+      const int cc = min(s * SC + j, C - 1);
+      const bool last = cc == C - 1;
+      const int dst = ((s & 1) * SC + j) * BUF;
+      const uint32_t ck = (uint32_t)cc * ROWB;
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        const int jj = wave + kMxWaves * i;
+        const int d = jj < KBS ? dst + jj * 1024 : dummy;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            g.ra, (__attribute__((address_space(3))) void*)(xs + d), 16, last ? xol[i] : xo[i],
+            ck, 0, 0);
+      }
+    }
+  };
+
+  f32x4_t acc[WT][NTT];
+#pragma unroll
+  for (int t = 0; t < WT; ++t) {
+    float b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * lg + i;
+      b[i] = (g.bias && r < g.rows_in[t]) ? g.bias[(size_t)g.e * g.N + g.tile_base[t] + r] : 0.0f;
+    }
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) acc[t][tt] = f32x4_t{b[0], b[1], b[2], b[3]};
+  }
+  constexpr int SRING = WRING / SC;   // scale groups in flight
+  u32x4_t wq[WRING][WT];
+  u32x4_t ws[SRING][WT];
+
+  __syncthreads();  // the previous pass is done with the LDS buffers
+  // the e8m0 scale rows of the pass's routed rows, row m at xsc + m * kGmScalePitch, its 16-byte
+  // piece p at slot p ^ gemm_swz8(m) (rows 128 bytes apart would otherwise put the scale bytes
+  // that 16 consecutive rows read together into one or two banks)
+  uint8_t* const xsc = xs + dummy + 1024;
+  static_assert(kGmScalePitch == 128, "8 pieces per staged scale row");
+  for (int j = wave; j < NTT * 2; j += kMxWaves) {   // 1 KB = 8 rows per instruction
+    const int m = j * 8 + lane / 8;
+    const int piece = (lane % 8) ^ gemm_swz8(m);
+    uint32_t off = kOOB;
+    if (m < g.live && piece * 16 < g.spa) {
+      const int r = g.row0 + g.p0 + m;
+      const uint32_t src = g.a_row ? (uint32_t)g.a_row[r] : (uint32_t)r;
+      off = src * (uint32_t)g.spa + piece * 16;
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        g.ras, (__attribute__((address_space(3))) void*)(xsc + j * 1024), 16, off, 0, 0, 0);
+  }
+  issue_fence();
+  load_x_super(0);
+  issue_fence();
+#pragma unroll
+  for (int j = 0; j < WRING; ++j) {
+    if (j % SC == 0) load_s(j / SC, ws[j / SC]);
+    load_w(j, wq[j]);
+    issue_fence();
+  }
+
+  const int swz = gemm_swz8(lr);
+  int cb = 0;   // first chunk of the loop trip
+  do {          // a do-while: C >= 1 (see gemm_pass)
+#pragma unroll
+    for (int sub = 0; sub < ITER / SC; ++sub) {
+      const int s = cb / SC + sub;
+      // after the DMA of super-chunk s: SC nibble chunks and one scale group
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(WT * SC + WT));
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      load_x_super(s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < SC; ++j) {
+        const int slot = (sub * SC + j) % WRING;
+        const int gslot = sub % SRING;
+        const int c = s * SC + j;
+        if (c < C) {
+          const uint8_t* xb = xs + ((s & 1) * SC + j) * BUF;
+          const bool kb_live = 4 * c + lg < g.KB;
+          int sa[WT];   // the MFMA reads the low byte
+#pragma unroll
+          for (int t = 0; t < WT; ++t) sa[t] = kb_live ? (int)(ws[gslot][t][j] >> (8 * lg)) : 0;
           const uint8_t* xb0 = xb + lr * ROWB + ((lg ^ swz) << 4);
           const uint8_t* xb1 = xb + lr * ROWB + (((4 + lg) ^ swz) << 4);
-          const uint8_t* sbp = xsc + lr * kGmScalePitch + 4 * c + lg;
+          // scale byte 4c + lg of row m: piece c / 4, byte 4 (c % 4) + lg (swizzled as staged)
+          const uint8_t* sbp =
+              xsc + lr * kGmScalePitch + (((c >> 2) ^ swz) << 4) + 4 * (c & 3) + lg;
           auto read_b = [&](int tt, i32x8_t& B, int& sb) {
             const u32x4_t b0 = *reinterpret_cast<const u32x4_t*>(xb0 + tt * 16 * ROWB);
             const u32x4_t b1 = *reinterpret_cast<const u32x4_t*>(xb1 + tt * 16 * ROWB);
@@ -296,92 +505,53 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
             const int sb = sbn;
             if (tt + 1 < NTT) read_b(tt + 1, Bn, sbn);
 #pragma unroll
-            for (int t = 0; t < kGmWT; ++t) {
-              const i32x8_t A = {(int)wq[sl][t][0], (int)wq[sl][t][1], (int)wq[sl][t][2],
-                                 (int)wq[sl][t][3], 0, 0, 0, 0};
+            for (int t = 0; t < WT; ++t) {
+              const i32x8_t A = {(int)wq[slot][t][0], (int)wq[slot][t][1], (int)wq[slot][t][2],
+                                 (int)wq[slot][t][3], 0, 0, 0, 0};
               acc[t][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                   A, B, acc[t][tt], kMfmaFmtFp4, kMfmaFmtFp8, 0, sa[t], 0, sb);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
-        } else {
-          float cs[kGmWT];
-#pragma unroll
-          for (int t = 0; t < kGmWT; ++t) cs[t] = e8m0_scale_operand(wx[sl][t]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            bf16x8_t A[kGmWT];
-#pragma unroll
-            for (int t = 0; t < kGmWT; ++t) A[t] = dequant8(wq[sl][t][i], cs[t]);
-#pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) {
-              const int m = tt * 16 + lr;   // m % 16 == lr
-              const bf16x8_t B =
-                  *reinterpret_cast<const bf16x8_t*>(xb + (m * 16 + ((lg * 4 + i) ^ swz)) * 16);
-#pragma unroll
-              for (int t = 0; t < kGmWT; ++t)
-                acc[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t], B, acc[t][tt], 0, 0, 0);
-            }
-          }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // refill in place: the nibble slot chunk c used, and after the super-chunk's last chunk
+        // its scale group (the same load counts in every super-chunk)
+        load_w(c + WRING, wq[slot]);
+        if (j == SC - 1) load_s(s + SRING, ws[gslot]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(c + kGmWRing, wq[sl], wx[sl]);   // refill the slot chunk c used, in place
-      __builtin_amdgcn_sched_barrier(0);
     }
-    c0 += kGmWRing;
-  } while (c0 < C);
+    cb += ITER;
+  } while (cb < C);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no LDS-DMA write outlives the pass
 
-  // epilogue: lane holds rows 4*lg..4*lg+3 of each weight tile for token column lr
-#pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) {
-    const int m = tt * 16 + lr;
-    if (m >= g.live) continue;
-    const size_t r = (size_t)(g.row0 + g.p0 + m);
-    if (swiglu) {
-#pragma unroll
-      for (int t = 0; t < 1; ++t) {
-        const int j0 = g.tile_base[t] + 4 * lg;
-        uint16_t h[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          h[i] = (uint16_t)f32_to_bf16_bits(
-              swiglu_oai(acc[t][tt][i], acc[t + 1][tt][i], g.alpha, g.limit));
-        uint16_t* dst = reinterpret_cast<uint16_t*>(g.out) + r * g.F + j0;
-        if (4 * lg + 4 <= g.rows_in[t] && (g.F & 3) == 0) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
-                                                      (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-        } else {
-          for (int i = 0; i < 4; ++i)
-            if (4 * lg + i < g.rows_in[t]) dst[i] = h[i];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < kGmWT; ++t) {
-        float* dst = reinterpret_cast<float*>(g.out) + r * g.N + g.tile_base[t] + 4 * lg;
-        if (4 * lg + 4 <= g.rows_in[t] && (g.N & 3) == 0) {
-          *reinterpret_cast<f32x4_t*>(dst) = acc[t][tt];
-        } else {
-          for (int i = 0; i < 4; ++i)
-            if (4 * lg + i < g.rows_in[t]) dst[i] = acc[t][tt][i];
-        }
-      }
-    }
-  }
+  gemm_epilogue<ACT, NTT, WT>(g, acc);
 }
 
+__host__ __device__ constexpr int gemm_threads(bool mx8) { return mx8 ? kMxThreads : kGmThreads; }
+
+// bf16: 8 wavefronts, 2 per SIMD (256 registers each); MXFP8: 4 wavefronts, 1 per SIMD, which
+// lets each use up to 512 registers (accumulators in AGPRs)
 template <int ACT, bool MX8>
-__global__ void __launch_bounds__(kGmThreads)
+__global__ void __launch_bounds__(gemm_threads(MX8), 1)
 gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int a_rows,
             const int32_t* __restrict__ a_row, const uint8_t* __restrict__ q,
             const uint8_t* __restrict__ s, const float* __restrict__ bias,
             const int32_t* __restrict__ counts, const int32_t* __restrict__ basep, int E, int N,
-            int K, float alpha, float limit, void* __restrict__ out) {
+            int K, float alpha, float limit, void* __restrict__ out, int nbx, int nslots,
+            int per_xcd) {
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  // XCD-aware tile order: the hardware deals workgroup ids to the 8 XCDs round robin, so id L
+  // runs on XCD L % 8; virtual tile v = (L % 8) * per_xcd + L / 8 gives every XCD a contiguous
+  // run of tiles, i.e. whole experts (bx fastest), and its L2 then holds the activation rows of
+  // the one or two experts it is working on instead of every expert's
+  const int L = (int)blockIdx.x;
+  const int v = (L % kXcds) * per_xcd + L / kXcds;
+  if (v >= nbx * nslots) return;
+  const int bxi = v % nbx, slot = v / nbx;
   const int c64 = ((int)(threadIdx.x & 63) < E) ? counts[threadIdx.x & 63] : 0;
-  const int e = wave_slot_expert(counts, E, (int)blockIdx.y, c64);
+  const int e = wave_slot_expert(counts, E, slot, c64);
   if (e < 0) return;   // uniform over the workgroup: fewer live experts than slots
   constexpr bool swiglu = (ACT == MOE_ACT_SWIGLU_OAI);
   GemmCtx g;
@@ -407,19 +577,25 @@ gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int
   g.row0 = basep[e];
   const int cnt = counts[e];
 
-  // weight rows of the wavefront's tiles (first row, rows that exist)
-  constexpr int kGmWT = gemm_wt(ACT);
+  // weight rows of the wavefront's tiles (first row, rows that exist). A workgroup covers 128
+  // h columns (SwiGLU: each wavefront's gate tiles [0, WT/2) and the matching up tiles) or 384
+  // rows (plain)
+  constexpr int kGmWT = MX8 ? mx_wt(ACT) : gemm_wt(ACT);
+  constexpr int kWaves = MX8 ? kMxWaves : kGmWaves;
 #pragma unroll
   for (int t = 0; t < kGmWT; ++t) {
     if (swiglu) {
-      const int jb = (int)blockIdx.x * 128 + wave * 16;   // tile 0: gate rows, tile 1: up rows
-      g.tile_base[t] = (t == 0) ? jb : g.F + jb;
+      constexpr int half = kGmWT / 2;
+      const int jb = bxi * 128 + wave * 16 * half + 16 * (t % half);
+      g.tile_base[t] = (t < half) ? jb : g.F + jb;
       g.rows_in[t] = min(16, g.F - jb);
     } else {
-      g.tile_base[t] = (int)blockIdx.x * (kGmWaves * kGmWT * 16) + (wave * kGmWT + t) * 16;
+      g.tile_base[t] = bxi * (kWaves * kGmWT * 16) + (wave * kGmWT + t) * 16;
       g.rows_in[t] = min(16, N - g.tile_base[t]);
     }
   }
+  static_assert(!swiglu || kWaves * kGmWT * 8 == 128, "128 h columns per workgroup");
+  static_assert(swiglu || kWaves * kGmWT * 16 == 384, "384 rows per workgroup");
 
   // buffer resources: this expert's nibbles and scales, and the activation rows
   const size_t ebase = (size_t)e * N * KB;   // first block of this expert (chunked layout)
@@ -436,6 +612,7 @@ gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int
     const uint32_t n = (uint32_t)(g.tile_base[t] + g.lr);
     const bool ok = g.lr < g.rows_in[t];
     g.so[t] = ok ? n * SP + g.lg : kOOB;
+    g.sg[t] = ok ? n * SP : kOOB;
     g.wo[t] = ok ? (n * kChunkBlocks + g.lg) * 16 : kOOB;
     g.wol[t] = (ok && g.lg < wlast) ? (n * wlast + g.lg) * 16 : kOOB;
   }
@@ -443,15 +620,28 @@ gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int
   for (int p0 = 0; p0 < cnt; p0 += kGmTT * 16) {
     g.p0 = p0;
     g.live = min(kGmTT * 16, cnt - p0);
-    switch ((g.live + 15) >> 4) {
-      case 1: gemm_pass<ACT, 1, MX8>(g, xs); break;
-      case 2: gemm_pass<ACT, 2, MX8>(g, xs); break;
-      case 3: gemm_pass<ACT, 3, MX8>(g, xs); break;
-      case 4: gemm_pass<ACT, 4, MX8>(g, xs); break;
-      case 5: gemm_pass<ACT, 5, MX8>(g, xs); break;
-      case 6: gemm_pass<ACT, 6, MX8>(g, xs); break;
-      case 7: gemm_pass<ACT, 7, MX8>(g, xs); break;
-      default: gemm_pass<ACT, 8, MX8>(g, xs); break;
+    if constexpr (MX8) {
+      switch ((g.live + 15) >> 4) {
+        case 1: gemm_pass_mx8<ACT, 1>(g, xs); break;
+        case 2: gemm_pass_mx8<ACT, 2>(g, xs); break;
+        case 3: gemm_pass_mx8<ACT, 3>(g, xs); break;
+        case 4: gemm_pass_mx8<ACT, 4>(g, xs); break;
+        case 5: gemm_pass_mx8<ACT, 5>(g, xs); break;
+        case 6: gemm_pass_mx8<ACT, 6>(g, xs); break;
+        case 7: gemm_pass_mx8<ACT, 7>(g, xs); break;
+        default: gemm_pass_mx8<ACT, 8>(g, xs); break;
+      }
+    } else {
+      switch ((g.live + 15) >> 4) {
+        case 1: gemm_pass<ACT, 1>(g, xs); break;
+        case 2: gemm_pass<ACT, 2>(g, xs); break;
+        case 3: gemm_pass<ACT, 3>(g, xs); break;
+        case 4: gemm_pass<ACT, 4>(g, xs); break;
+        case 5: gemm_pass<ACT, 5>(g, xs); break;
+        case 6: gemm_pass<ACT, 6>(g, xs); break;
+        case 7: gemm_pass<ACT, 7>(g, xs); break;
+        default: gemm_pass<ACT, 8>(g, xs); break;
+      }
     }
   }
 }
@@ -485,14 +675,18 @@ int gemm_launch(const void* a, const uint8_t* a_scale, const int32_t* a_row, int
     lds_attr_set = true;
   }
   const int lds = gemm_lds_bytes(MX8);
-  const dim3 grid((unsigned)bx, (unsigned)slots), block(kGmThreads);
+  // a 1-D grid of tiles (weight-row slice bx, expert slot), ordered per XCD in the kernel
+  const int64_t tiles = bx * slots;
+  const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
+  const dim3 grid((unsigned)(per_xcd * kXcds)), block(gemm_threads(MX8));
   if (act == MOE_ACT_SWIGLU_OAI)
     launch(gemm_kernel<MOE_ACT_SWIGLU_OAI, MX8>, grid, block, lds, stream, a, a_scale,
            (int)a_rows, a_row, w->q, w->s, w->bias, counts, basep, w->E, w->N, w->K, alpha,
-           limit, out);
+           limit, out, (int)bx, (int)slots, (int)per_xcd);
   else
     launch(gemm_kernel<MOE_ACT_NONE, MX8>, grid, block, lds, stream, a, a_scale, (int)a_rows,
-           a_row, w->q, w->s, w->bias, counts, basep, w->E, w->N, w->K, alpha, limit, out);
+           a_row, w->q, w->s, w->bias, counts, basep, w->E, w->N, w->K, alpha, limit, out,
+           (int)bx, (int)slots, (int)per_xcd);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 

@@ -15,9 +15,9 @@
 //    E read zeros.
 //  * top-k: one wavefront per token on the LDS logits row (the moe_route_topk code).
 //  * bucket: the CSR needs every token's ids, so the LAST workgroup to finish its tokens builds
-//    it: each workgroup publishes its ids (device-scope release fence) and increments a
-//    caller-provided counter; the one that brings it to the grid size acquires, copies all ids
-//    into LDS, histograms them, scans the padded counts into basep, and compacts each expert's
+//    it: each workgroup stores its ids with device-scope atomic stores, waits for them to be
+//    acknowledged and increments a caller-provided counter; the one that brings it to the grid
+//    size reads every id with device-scope atomic loads, copies them into LDS, histograms them, scans the padded counts into basep, and compacts each expert's
 //    rows in ascending token order (each wavefront owns whole experts, one ballot per 64
 //    tokens), then resets the counter to zero. No workgroup ever waits for another.
 #include "route_core.hpp"
@@ -71,25 +71,25 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const uint32_t ao = e_row < E ? ((uint32_t)e_row * D + 8 * lg) * 2 : kOOB;
     const uint32_t bo = t0 + lr < T ? ((uint32_t)(t0 + lr) * D + 8 * lg) * 2 : kOOB;
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    int s = s0;
-    for (; s + 1 < s1; s += 2) {   // two independent chains
-      const u32x4_t a0 = buf_load16(rw, ao, (uint32_t)s * 64), b0 = buf_load16(rx, bo, (uint32_t)s * 64);
-      const u32x4_t a1 = buf_load16(rw, ao, (uint32_t)s * 64 + 64);
-      const u32x4_t b1 = buf_load16(rx, bo, (uint32_t)s * 64 + 64);
-      bf16x8_t A0, B0, A1, B1;
-      __builtin_memcpy(&A0, &a0, 16);
-      __builtin_memcpy(&B0, &b0, 16);
-      __builtin_memcpy(&A1, &a1, 16);
-      __builtin_memcpy(&B1, &b1, 16);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B1, acc1, 0, 0, 0);
-    }
-    if (s < s1) {
-      const u32x4_t a0 = buf_load16(rw, ao, (uint32_t)s * 64), b0 = buf_load16(rx, bo, (uint32_t)s * 64);
-      bf16x8_t A0, B0;
-      __builtin_memcpy(&A0, &a0, 16);
-      __builtin_memcpy(&B0, &b0, 16);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, acc0, 0, 0, 0);
+    // 8 k steps per round: all 16 loads in flight before the MFMAs (steps past s1 read zeros)
+    for (int sb = s0; sb < s1; sb += 8) {
+      u32x4_t a[8], b[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool ok = sb + i < s1;
+        a[i] = buf_load16(rw, ok ? ao : kOOB, (uint32_t)(sb + i) * 64);
+        b[i] = buf_load16(rx, ok ? bo : kOOB, (uint32_t)(sb + i) * 64);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        bf16x8_t A, B;
+        __builtin_memcpy(&A, &a[i], 16);
+        __builtin_memcpy(&B, &b[i], 16);
+        if (i & 1)
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc1, 0, 0, 0);
+        else
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc0, 0, 0, 0);
+      }
     }
     // lane holds experts tile*16 + 4*lg + i of token lr
 #pragma unroll
@@ -114,16 +114,30 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     int my_id;
     float my_v;
     wave_topk(part + (size_t)wave * E, E, k, my_id, my_v);
-    write_topk(my_id, my_v, k, ids + (size_t)(t0 + wave) * k, w + (size_t)(t0 + wave) * k);
+    // the softmax weights as in write_topk; the ids are stored with device-scope atomic stores,
+    // which bypass the XCD's non-coherent L2, so that another XCD's workgroup can read them
+    const float v0 = __shfl(my_v, 0);
+    double den = 0.0;
+    for (int r = 0; r < k; ++r) den += exp((double)__shfl(my_v, r) - (double)v0);
+    if (lane < k) {
+      __hip_atomic_store(ids + (size_t)(t0 + wave) * k + lane, my_id, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      w[(size_t)(t0 + wave) * k + lane] = (float)(exp((double)my_v - (double)v0) / den);
+    }
   }
 
   // ---- the last workgroup builds the CSR ----
-  __threadfence();   // release: this workgroup's ids before its count
+  // Every wavefront waits until its stores are acknowledged, then the workgroup counts itself
+  // in; the one that completes the count reads the ids with device-scope atomic loads. (A
+  // device-scope fence would also work but writes back and invalidates the whole L2, which
+  // costs microseconds per workgroup.)
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(sync, 1u) == gridDim.x - 1;
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();   // acquire: every workgroup's ids
 
   const int R = T * k;
   int* hist = reinterpret_cast<int*>(smem);
@@ -132,7 +146,7 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
   for (int i = tid; i < E; i += kRtThreads) hist[i] = 0;
   __syncthreads();
   for (int i = tid; i < R; i += kRtThreads) {
-    const int id = ids[i];
+    const int id = __hip_atomic_load(ids + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     idl[i] = id;
     if ((unsigned)id < (unsigned)E) atomicAdd(&hist[id], 1);
   }
@@ -182,7 +196,8 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     for (int r = b + running + lane; r < b + pe; r += 64) row_tok[r] = -1;   // padding rows
   }
   for (int r = total + tid; r < mpad_max; r += kRtThreads) row_tok[r] = -1;   // ghost rows
-  if (tid == 0) atomicExch(sync, 0u);   // ready for the next call
+  if (tid == 0)   // ready for the next call
+    __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace moe

@@ -230,7 +230,7 @@ def test_one_hot_decode_sweep_mx8():
 
 
 @pytest.mark.parametrize("N,K,act", [(40, 64, NONE), (36, 64, SWIGLU), (264, 96, NONE),
-                                     (2 * 130, 64, SWIGLU), (8, 32, NONE), (400, 8192, NONE)])
+                                     (2 * 130, 64, SWIGLU), (8, 32, NONE), (400, 4096, NONE)])
 def test_projection_ragged_n_mx8(N, K, act):
     E, T, k, tile_m = 3, 25, 2, 16
     W = synth.random_mx4(N + K, E, N, K)
