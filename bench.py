@@ -123,6 +123,15 @@ class Layer:
                            m.MOE_ACT_NONE, 1.702, 7.0, out=self.d)
         self.combine()
 
+    def decode_persistent(self, ws):
+        """The chain as mx4_moe_decode_persistent (one launch)."""
+        c = self.csr
+        self.moe.mx4_moe_decode_persistent(self.logits, self.x, self.GU, self.DN, self.wl.k, ws,
+                                           1.702, 7.0,
+                                           out={"ids": self.ids, "w": self.w, "counts": c[0],
+                                                "basep": c[1], "row_tok": c[2], "pos": c[3],
+                                                "h": self.h, "y": self.y})
+
     def decode(self):
         """The chain as mx4_moe_decode (two launches; h in routed-row order, T*k rows)."""
         c = self.csr

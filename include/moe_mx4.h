@@ -20,6 +20,8 @@
  * and, for decode (a few tokens), the same chain fused into two launches:
  *
  *   mx4_moe_decode  logits + x -> routing, CSR, h, (d), y
+ *   mx4_moe_decode_persistent  the same in one launch (a resident grid; down weights stream
+ *                   while gate_up is still running)
  *
  * Sources (web pages on the daScript repository's dasLLAMA engine; cited by tag below):
  *   [fusion]  PR #3579 "dasLLAMA gpt-oss arc", commit log, the Metal fusion-lane commit: the
@@ -307,6 +309,33 @@ int mx4_moe_decode(const float* logits, const uint16_t* x, int64_t T, int E, int
                    const mx4_experts* w_gu, const mx4_experts* w_dn, float alpha, float limit,
                    int32_t* ids, float* w, int32_t* counts, int32_t* basep, int32_t* row_tok,
                    int32_t* pos, uint16_t* h, float* d, float* y, void* stream);
+
+#define MOE_DECODE_WS_WORDS 32   /* u32 workspace words of mx4_moe_decode_persistent */
+
+/*
+ * The same chain as mx4_moe_decode in ONE launch ([chain]'s two stages without the launch
+ * boundary between them): a grid of workgroups that can all be resident at once runs the
+ * gate_up items (as launch 1) and then the down items (as launch 2); a down item starts
+ * streaming its expert rows as soon as it has routed its token and then waits, on a per-token
+ * counter, for that token's h rows. Outputs and layouts are those of mx4_moe_decode; routing
+ * and the CSR are identical bit for bit, h, d and y within the same tolerances (the gate_up K
+ * split is chosen for the grid, so fp32 sums may associate differently; at a given grid the
+ * results are deterministic).
+ *   ws    u32 [MOE_DECODE_WS_WORDS] device workspace owned by the caller: zero before the first
+ *         call; every call leaves words 0..2 and 4.. zero again. Calls that can run
+ *         concurrently need distinct workspaces. Word 3 is an error flag the call sets (and
+ *         never clears) if a wait ran past its bound (about a second); the outputs of that call
+ *         are then invalid. This cannot happen while the grid is resident as sized here.
+ *   max_workgroups  0, or a cap on the grid (at least 1) for callers sharing the GPU.
+ * Errors: those of mx4_moe_decode, plus MOE_EINVAL for ws == NULL or max_workgroups < 0,
+ *         MOE_EALIGN for ws not 4-byte aligned, MOE_ELAUNCH if the occupancy query fails.
+ */
+int mx4_moe_decode_persistent(const float* logits, const uint16_t* x, int64_t T, int E, int k,
+                              const mx4_experts* w_gu, const mx4_experts* w_dn, float alpha,
+                              float limit, int32_t* ids, float* w, int32_t* counts,
+                              int32_t* basep, int32_t* row_tok, int32_t* pos, uint16_t* h,
+                              float* d, float* y, uint32_t* ws, int max_workgroups,
+                              void* stream);
 
 /*
  * Router-weighted combine ([chain]: routing-weighted sum of the expert rows in slot order).

@@ -19,7 +19,9 @@ MOE_MAX_K, MOE_MAX_E, MOE_MAX_TILE_M = 16, 1024, 256
 
 EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_pack_experts",
            "mx4_moe_gemv", "mx4_moe_gemm", "moe_combine", "mx4_moe_decode", "moe_timing_arm",
-           "moe_timing_read", "mx8_quantize", "mx4_moe_gemm_mx8", "moe_router")
+           "moe_timing_read", "mx8_quantize", "mx4_moe_gemm_mx8", "moe_router",
+           "mx4_moe_decode_persistent")
+MOE_DECODE_WS_WORDS = 32
 MOE_ROUTER_MAX_ROUTED = 16384
 MOE_MX8_GEMM_MAX_K = 4096
 
@@ -71,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.mx4_moe_decode.restype = ci
         L.mx4_moe_decode.argtypes = [vp, vp, i64, ci, ci, pe, pe, cf, cf,
                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.mx4_moe_decode_persistent.restype = ci
+        L.mx4_moe_decode_persistent.argtypes = [vp, vp, i64, ci, ci, pe, pe, cf, cf, vp, vp, vp,
+                                                vp, vp, vp, vp, vp, vp, vp, ci, vp]
         L.moe_router.restype = ci
         L.moe_router.argtypes = [vp, vp, vp, i64, ci, ci, ci, ci, i64, vp, vp, vp, vp, vp, vp,
                                  vp, vp, vp]
@@ -361,6 +366,34 @@ def mx4_moe_decode(logits, x, gate_up: MX4Experts, down: MX4Experts, k: int,
           ctypes.byref(down.c), float(alpha), float(limit), _ptr(o["ids"]), _ptr(o["w"]),
           _ptr(o["counts"]), _ptr(o["basep"]), _ptr(o["row_tok"]), _ptr(o["pos"]), _ptr(o["h"]),
           _ptr(o.get("d")), _ptr(o["y"]), _stream(stream))
+    return o
+
+
+def mx4_moe_decode_persistent(logits, x, gate_up: MX4Experts, down: MX4Experts, k: int, ws,
+                              alpha: float = 1.702, limit: float = 7.0, want_d: bool = False,
+                              out=None, max_workgroups: int = 0, stream=None):
+    """mx4_moe_decode in one launch. ws: a zeroed int32 device tensor of MOE_DECODE_WS_WORDS
+    words (left zero; word 3 is the error flag). Same outputs as mx4_moe_decode."""
+    torch = _torch()
+    _check(logits, torch.float32, "logits")
+    _check(x, torch.bfloat16, "x")
+    T, E = logits.shape
+    D, F = gate_up.K, gate_up.N // 2
+    dev = logits.device
+    o = dict(out or {})
+    shapes = {"ids": ((T, k), torch.int32), "w": ((T, k), torch.float32),
+              "counts": ((E,), torch.int32), "basep": ((E + 1,), torch.int32),
+              "row_tok": ((T * k,), torch.int32), "pos": ((T, k), torch.int32),
+              "h": ((T * k, F), torch.bfloat16), "y": ((T, D), torch.float32)}
+    if want_d:
+        shapes["d"] = ((T * k, D), torch.float32)
+    for key, (shape, dt) in shapes.items():
+        if key not in o:
+            o[key] = torch.empty(shape, dtype=dt, device=dev)
+    _call("mx4_moe_decode_persistent", _ptr(logits), _ptr(x), T, E, k, ctypes.byref(gate_up.c),
+          ctypes.byref(down.c), float(alpha), float(limit), _ptr(o["ids"]), _ptr(o["w"]),
+          _ptr(o["counts"]), _ptr(o["basep"]), _ptr(o["row_tok"]), _ptr(o["pos"]), _ptr(o["h"]),
+          _ptr(o.get("d")), _ptr(o["y"]), _ptr(ws), int(max_workgroups), _stream(stream))
     return o
 
 

@@ -118,15 +118,23 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
 // Routing weights of the picks held by lanes 0..k-1 (wave_topk): lane 0 sums exp(v_r - v_0) in
 // double in pick order, then writes ids[r] and w[r] = f32(exp(v_r - v_0) / sum) for r < k.
 // Every lane must call it (it shuffles).
-__device__ __forceinline__ void write_topk(int my_id, float my_v, int k, int32_t* __restrict__ ids,
-                                           float* __restrict__ w) {
-  const int lane = (int)(threadIdx.x & 63);
+// Routing weight of the pick held by this lane (lanes 0..k-1 of wave_topk): the softmax over the
+// k picks, summed in double in pick order relative to pick 0, rounded to f32. Every lane must
+// call it (it shuffles); lanes >= k get a value of no meaning.
+__device__ __forceinline__ float topk_weight(float my_v, int k) {
   const float v0 = __shfl(my_v, 0);
   double den = 0.0;
   for (int r = 0; r < k; ++r) den += exp((double)__shfl(my_v, r) - (double)v0);
+  return (float)(exp((double)my_v - (double)v0) / den);
+}
+
+__device__ __forceinline__ void write_topk(int my_id, float my_v, int k, int32_t* __restrict__ ids,
+                                           float* __restrict__ w) {
+  const int lane = (int)(threadIdx.x & 63);
+  const float wt = topk_weight(my_v, k);
   if (lane < k) {
     ids[lane] = my_id;
-    w[lane] = (float)(exp((double)my_v - (double)v0) / den);
+    w[lane] = wt;
   }
 }
 

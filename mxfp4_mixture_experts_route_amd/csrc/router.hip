@@ -114,15 +114,13 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     int my_id;
     float my_v;
     wave_topk(part + (size_t)wave * E, E, k, my_id, my_v);
-    // the softmax weights as in write_topk; the ids are stored with device-scope atomic stores,
-    // which bypass the XCD's non-coherent L2, so that another XCD's workgroup can read them
-    const float v0 = __shfl(my_v, 0);
-    double den = 0.0;
-    for (int r = 0; r < k; ++r) den += exp((double)__shfl(my_v, r) - (double)v0);
+    // the ids are stored with device-scope atomic stores, which bypass the XCD's non-coherent
+    // L2, so that another XCD's workgroup can read them
+    const float wt = topk_weight(my_v, k);
     if (lane < k) {
       __hip_atomic_store(ids + (size_t)(t0 + wave) * k + lane, my_id, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-      w[(size_t)(t0 + wave) * k + lane] = (float)(exp((double)my_v - (double)v0) / den);
+      w[(size_t)(t0 + wave) * k + lane] = wt;
     }
   }
 

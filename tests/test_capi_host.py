@@ -233,3 +233,20 @@ def test_router_argument_checks():
     assert call(mpad=7) == _lib.MOE_ESHAPE
     assert call(x=ctypes.c_void_p(0x1008)) == _lib.MOE_EALIGN
     assert call(w_r=ctypes.c_void_p(0x1004)) == _lib.MOE_EALIGN
+
+
+@no_gpu
+def test_decode_persistent_argument_checks():
+    f = _lib.lib().mx4_moe_decode_persistent
+    gu, dn = experts(E=8, N=128, K=64), experts(E=8, N=64, K=64)
+
+    def call(ws=FAKE, max_wg=0, T=2, k=2, gu=gu, dn=dn):
+        return f(FAKE, FAKE, T, 8, k, ctypes.byref(gu), ctypes.byref(dn), 1.702, 7.0, FAKE, FAKE,
+                 FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, max_wg, None)
+
+    assert call(ws=None) == _lib.MOE_EINVAL
+    assert call(max_wg=-1) == _lib.MOE_EINVAL
+    assert call(T=0) == _lib.MOE_EINVAL
+    assert call(T=17) == _lib.MOE_ESHAPE
+    assert call(dn=experts(E=8, N=32, K=64)) == _lib.MOE_ESHAPE
+    assert call(ws=ctypes.c_void_p(0x1002)) == _lib.MOE_EALIGN
