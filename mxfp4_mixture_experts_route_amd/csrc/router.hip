@@ -51,6 +51,7 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
               uint32_t* __restrict__ sync) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_last;
+  __shared__ int s_ids[kRtTok * MOE_MAX_K];   // this workgroup's picks (the one-workgroup case)
   __shared__ int s_wave_tot[kRtWaves];
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
@@ -121,6 +122,7 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
       __hip_atomic_store(ids + (size_t)(t0 + wave) * k + lane, my_id, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
       w[(size_t)(t0 + wave) * k + lane] = wt;
+      s_ids[wave * k + lane] = my_id;
     }
   }
 
@@ -129,13 +131,19 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
   // in; the one that completes the count reads the ids with device-scope atomic loads. (A
   // device-scope fence would also work but writes back and invalidates the whole L2, which
   // costs microseconds per workgroup.)
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             gridDim.x - 1;
-  __syncthreads();
-  if (!s_last) return;
+  // (A grid of one workgroup is the last by itself and has every id in LDS already.)
+  const bool alone = gridDim.x == 1;
+  if (!alone) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               gridDim.x - 1;
+    __syncthreads();
+    if (!s_last) return;
+  } else {
+    __syncthreads();
+  }
 
   const int R = T * k;
   int* hist = reinterpret_cast<int*>(smem);
@@ -144,7 +152,8 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
   for (int i = tid; i < E; i += kRtThreads) hist[i] = 0;
   __syncthreads();
   for (int i = tid; i < R; i += kRtThreads) {
-    const int id = __hip_atomic_load(ids + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int id = alone ? s_ids[i]
+                         : __hip_atomic_load(ids + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     idl[i] = id;
     if ((unsigned)id < (unsigned)E) atomicAdd(&hist[id], 1);
   }
@@ -194,7 +203,7 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     for (int r = b + running + lane; r < b + pe; r += 64) row_tok[r] = -1;   // padding rows
   }
   for (int r = total + tid; r < mpad_max; r += kRtThreads) row_tok[r] = -1;   // ghost rows
-  if (tid == 0)   // ready for the next call
+  if (tid == 0 && !alone)   // ready for the next call
     __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
