@@ -69,7 +69,11 @@ typedef enum {
 
 typedef enum {
   MOE_ACT_NONE = 0,       /* out = f32 [mpad_max][N]: bias + a . W^T                              */
-  MOE_ACT_SWIGLU_OAI = 1  /* out = bf16 [mpad_max][N/2]: clamped SwiGLU-OAI of (gate, up) halves */
+  MOE_ACT_SWIGLU_OAI = 1, /* out = bf16 [mpad_max][N/2]: clamped SwiGLU-OAI of (gate, up) halves */
+  MOE_ACT_SWIGLU_OAI_MX8 = 2 /* mx4_moe_gemm_mx8 only: the SwiGLU-OAI rows, rounded to bf16, then
+                                written as MXFP8 rows (out: E4M3 [mpad_max][N/2], out_scale:
+                                e8m0 [mpad_max][roundup(N/64, 16)]), bit for bit what
+                                mx8_quantize makes of the bf16 rows                           */
 } moe_act;
 
 #define MOE_MAX_K 16        /* experts per token */
@@ -263,9 +267,14 @@ int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b_r, int64_t
  * (products are exact; the hardware's sum over a 128-value step is not rounded like a chain of
  * fp32 additions but stays within the same error bound, |error| <= 1e-3 * sum |x_i W_i|).
  * Arguments, row semantics, epilogue (MOE_ACT_NONE / MOE_ACT_SWIGLU_OAI) and outputs as
- * mx4_moe_gemm; a_rows counts MXFP8 rows.
+ * mx4_moe_gemm; a_rows counts MXFP8 rows. MOE_ACT_SWIGLU_OAI_MX8 writes the SwiGLU-OAI rows
+ * directly as MXFP8 rows (out: E4M3 bytes, out_scale: e8m0 rows with zero padding), the input
+ * format of the down projection, so the bf16 rows never leave the chip; out_scale is unused
+ * (may be NULL) otherwise.
  * Errors: as mx4_moe_gemm (aq in place of a, also NULL as), plus MOE_ESHAPE for
- *         K > MOE_MX8_GEMM_MAX_K and MOE_EALIGN for as not 16-byte aligned.
+ *         K > MOE_MX8_GEMM_MAX_K, MOE_EINVAL for MOE_ACT_SWIGLU_OAI_MX8 with out_scale NULL,
+ *         MOE_ESHAPE for it with N % 64 != 0, MOE_EALIGN for as or out_scale not 16-byte
+ *         aligned.
  */
 #define MOE_MX8_GEMM_MAX_K 4096  /* reduction length of mx4_moe_gemm_mx8 (LDS scale staging) */
 
@@ -275,7 +284,7 @@ int mx8_quantize(const uint16_t* a, const int32_t* live, int64_t rows, int K, ui
 int mx4_moe_gemm_mx8(const uint8_t* aq, const uint8_t* as, const int32_t* a_row, int64_t a_rows,
                      const mx4_experts* w, const int32_t* counts, const int32_t* basep, int tile_m,
                      int64_t mpad_max, int act, float alpha, float limit, void* out,
-                     void* stream);
+                     uint8_t* out_scale, void* stream);
 
 #define MOE_DECODE_MAX_T 16  /* tokens per mx4_moe_decode call */
 #define MOE_DECODE_MAX_K 8   /* experts per token in mx4_moe_decode */

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_mx4.so")
 
 MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_ELAUNCH = 0, 1, 2, 3, 4
-MOE_ACT_NONE, MOE_ACT_SWIGLU_OAI = 0, 1
+MOE_ACT_NONE, MOE_ACT_SWIGLU_OAI, MOE_ACT_SWIGLU_OAI_MX8 = 0, 1, 2
 MOE_MAX_K, MOE_MAX_E, MOE_MAX_TILE_M = 16, 1024, 256
 
 EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_pack_experts",
@@ -83,7 +83,7 @@ def lib() -> ctypes.CDLL:
         L.mx8_quantize.argtypes = [vp, vp, i64, ci, vp, vp, vp]
         L.mx4_moe_gemm_mx8.restype = ci
         L.mx4_moe_gemm_mx8.argtypes = [vp, vp, vp, i64, ctypes.POINTER(Mx4ExpertsC), vp, vp, ci,
-                                       i64, ci, cf, cf, vp, vp]
+                                       i64, ci, cf, cf, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -306,8 +306,9 @@ def mx8_quantize(a, live=None, out=None, stream=None):
 
 
 def mx4_moe_gemm_mx8(aq, as_, a_row, w, counts, basep, tile_m, mpad_max, act=MOE_ACT_NONE,
-                     alpha=1.702, limit=7.0, out=None, stream=None):
-    """mx4_moe_gemm over MXFP8 activation rows (aq, as_) from mx8_quantize."""
+                     alpha=1.702, limit=7.0, out=None, out_scale=None, stream=None):
+    """mx4_moe_gemm over MXFP8 activation rows (aq, as_) from mx8_quantize. With
+    MOE_ACT_SWIGLU_OAI_MX8 the SwiGLU rows come out as MXFP8 rows: returns (q, s)."""
     torch = _torch()
     _check(aq, torch.uint8, "aq")
     _check(as_, torch.uint8, "as")
@@ -315,15 +316,22 @@ def mx4_moe_gemm_mx8(aq, as_, a_row, w, counts, basep, tile_m, mpad_max, act=MOE
         _check(a_row, torch.int32, "a_row")
     _check(counts, torch.int32, "counts")
     _check(basep, torch.int32, "basep")
-    if out is None:
+    if act == MOE_ACT_SWIGLU_OAI_MX8:
+        F = w.N // 2
+        if out is None:
+            out = torch.empty((mpad_max, F), dtype=torch.uint8, device=aq.device)
+        if out_scale is None:
+            out_scale = torch.empty((mpad_max, scale_row_bytes(F)), dtype=torch.uint8,
+                                    device=aq.device)
+    elif out is None:
         if act == MOE_ACT_SWIGLU_OAI:
             out = torch.empty((mpad_max, w.N // 2), dtype=torch.bfloat16, device=aq.device)
         else:
             out = torch.empty((mpad_max, w.N), dtype=torch.float32, device=aq.device)
     _call("mx4_moe_gemm_mx8", _ptr(aq), _ptr(as_), _ptr(a_row), aq.shape[0], ctypes.byref(w.c),
           _ptr(counts), _ptr(basep), tile_m, mpad_max, act, float(alpha), float(limit),
-          _ptr(out), _stream(stream))
-    return out
+          _ptr(out), _ptr(out_scale), _stream(stream))
+    return (out, out_scale) if act == MOE_ACT_SWIGLU_OAI_MX8 else out
 
 
 def moe_combine(d, pos, w, out=None, stream=None):
@@ -413,7 +421,8 @@ def moe_layer(x, logits, gate_up: MX4Experts, down: MX4Experts, k: int, tile_m: 
               alpha: float = 1.702, limit: float = 7.0, projection: str = "gemm", stream=None):
     """One routed-expert MoE layer: route -> bucket -> gate_up+SwiGLU -> down -> combine.
     projection: "gemm" or "gemv" (bf16 activations), or "gemm_mx8" (MXFP8 activations on the
-    MX-scaled MFMA: x quantized once, h quantized after the SwiGLU; adds xq/xs/hq/hs).
+    MX-scaled MFMA: x quantized once, h written as MXFP8 rows by the gate_up epilogue; returns
+    xq/xs/hq/hs and no bf16 h).
     Returns a dict of every intermediate (device tensors)."""
     if projection not in ("gemm", "gemv", "gemm_mx8"):
         raise ValueError(f"unknown projection {projection!r}")
@@ -424,11 +433,11 @@ def moe_layer(x, logits, gate_up: MX4Experts, down: MX4Experts, k: int, tile_m: 
     extra = {}
     if projection == "gemm_mx8":
         xq, xs = mx8_quantize(x, stream=stream)
-        h = mx4_moe_gemm_mx8(xq, xs, row_tok, gate_up, counts, basep, tile_m, mpad,
-                             MOE_ACT_SWIGLU_OAI, alpha, limit, stream=stream)
-        hq, hs = mx8_quantize(h, live=row_tok, stream=stream)
+        hq, hs = mx4_moe_gemm_mx8(xq, xs, row_tok, gate_up, counts, basep, tile_m, mpad,
+                                  MOE_ACT_SWIGLU_OAI_MX8, alpha, limit, stream=stream)
         d = mx4_moe_gemm_mx8(hq, hs, None, down, counts, basep, tile_m, mpad, MOE_ACT_NONE,
                              alpha, limit, stream=stream)
+        h = None
         extra = {"xq": xq, "xs": xs, "hq": hq, "hs": hs}
     else:
         fn = mx4_moe_gemm if projection == "gemm" else mx4_moe_gemv

@@ -12,7 +12,7 @@ int moe_launch_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, con
 int moe_launch_gemm_mx8(const uint8_t* aq, const uint8_t* as, const int32_t* a_row,
                         int64_t a_rows, const mx4_experts* w, const int32_t* counts,
                         const int32_t* basep, int tile_m, int64_t mpad_max, int act, float alpha,
-                        float limit, void* out, hipStream_t stream);
+                        float limit, void* out, uint8_t* out_scale, hipStream_t stream);
 
 namespace {
 
@@ -69,12 +69,17 @@ extern "C" int mx4_moe_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_r
 extern "C" int mx4_moe_gemm_mx8(const uint8_t* aq, const uint8_t* as, const int32_t* a_row,
                                 int64_t a_rows, const mx4_experts* w, const int32_t* counts,
                                 const int32_t* basep, int tile_m, int64_t mpad_max, int act,
-                                float alpha, float limit, void* out, void* stream) {
+                                float alpha, float limit, void* out, uint8_t* out_scale,
+                                void* stream) {
   if (!as) return MOE_EINVAL;
-  const int st = check_projection(aq, a_row, a_rows, w, counts, basep, tile_m, mpad_max, act, out);
+  const bool q_out = act == MOE_ACT_SWIGLU_OAI_MX8;
+  if (q_out && !out_scale) return MOE_EINVAL;
+  // the MXFP8 output takes the SwiGLU shape checks
+  const int st = check_projection(aq, a_row, a_rows, w, counts, basep, tile_m, mpad_max,
+                                  q_out ? MOE_ACT_SWIGLU_OAI : act, out);
   if (st != MOE_OK) return st;
-  if (w->K > MOE_MX8_GEMM_MAX_K) return MOE_ESHAPE;
-  if (((uintptr_t)as) & 15) return MOE_EALIGN;
+  if (w->K > MOE_MX8_GEMM_MAX_K || (q_out && w->N % 64 != 0)) return MOE_ESHAPE;
+  if ((((uintptr_t)as) & 15) || (q_out && (((uintptr_t)out_scale) & 15))) return MOE_EALIGN;
   return moe_launch_gemm_mx8(aq, as, a_row, a_rows, w, counts, basep, tile_m, mpad_max, act, alpha,
-                             limit, out, (hipStream_t)stream);
+                             limit, out, out_scale, (hipStream_t)stream);
 }

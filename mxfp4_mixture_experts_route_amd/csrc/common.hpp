@@ -102,6 +102,37 @@ __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) {
   return r;
 }
 
+// E4M3 byte of a finite fp32 value t with |t| < 2^9, round to nearest even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float t) {
+  const uint32_t u = __float_as_uint(t);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t mag;
+  if (a < 0x3C800000u) {                      // |t| < 2^-6: subnormal step 2^-9
+    // |t| * 2^9 < 8 is exact; rintf rounds half to even; 8 lands on 2^-6 = byte 0x08
+    mag = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    // keep 3 mantissa bits, rounding half to even (a carry into the exponent is a correct
+    // round up to the next binade)
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    const int ex = (int)(r >> 23) - 127;      // >= -6
+    const uint32_t m3 = (r >> 20) & 7u;
+    mag = (ex > 8 || (ex == 8 && m3 == 7u)) ? 0x7Eu : ((uint32_t)(ex + 7) << 3) | m3;
+  }
+  return sign | mag;
+}
+
+// MXFP8 scale byte of a 32-value block whose largest magnitude, as a bf16 pattern with the sign
+// cleared, is amax (OCP MX: exponent of the maximum minus 8, clamped at e8m0 byte 0), and the
+// exact factor 2^-X that scales the block's values onto the E4M3 grid.
+__device__ __forceinline__ uint32_t mx8_scale_byte(uint32_t amax) {
+  const int ea = (int)(amax >> 7);
+  return (uint32_t)max(ea - 8, 0);
+}
+__device__ __forceinline__ float mx8_inv_scale(uint32_t sbyte) {
+  return __uint_as_float((254u - sbyte) << 23);   // 2^(127 - sbyte), a normal float
+}
+
 // Clamped SwiGLU-OAI of one (gate, up) pair: gc = min(gate, limit), uc = clamp(up, +-limit),
 // gc * sigmoid(alpha*gc) * (uc + 1). The sigmoid is evaluated on the side where exp() cannot
 // overflow, so very negative gates give correctly tiny (not zero-by-overflow) results.

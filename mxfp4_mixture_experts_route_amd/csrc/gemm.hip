@@ -103,6 +103,8 @@ struct GemmCtx {
   const float* bias;
   void* out;
   const uint8_t* a_scale;   // MXFP8 activation scale rows (pitch spa), else unused
+  uint8_t* out_scale;       // MOE_ACT_SWIGLU_OAI_MX8: e8m0 rows of h (pitch spo)
+  int spo;
   __amdgpu_buffer_rsrc_t rq, rs, ra, ras;
   int e, N, K, KB, C, klast, row0, p0, live, F, spa;
   int tid, lr, lg;
@@ -120,6 +122,51 @@ __device__ __forceinline__ void gemm_epilogue(const GemmCtx& g, const f32x4_t (&
   constexpr bool swiglu = (ACT == MOE_ACT_SWIGLU_OAI);
   constexpr int kGmWT = WT;
   const int lr = g.lr, lg = g.lg;
+  if constexpr (ACT == MOE_ACT_SWIGLU_OAI_MX8) {
+    // MXFP8 rows of h: with 4 tiles per wavefront its 32 h columns [jb, jb + 32) (gate tiles 0
+    // and 1, up tiles 2 and 3) are one MX block per token row, held by the 4 lanes of a token
+    // column (lg = 0..3, 8 values each): the block maximum takes two cross-lane steps. Values
+    // are the bf16-rounded SwiGLU-OAI outputs, scaled and encoded as mx8_quantize does.
+    static_assert(WT == 4, "one 32-column block per wavefront");
+    const int jb = g.tile_base[0];
+    const bool cols_live = jb < g.F;                 // F % 32 == 0: the block is whole or absent
+    const int blk = jb >> 5, nblk = g.F >> 5;
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      const int m = tt * 16 + lr;
+      uint32_t hb[2][4];
+      uint32_t amax = 0;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hb[t][i] = f32_to_bf16_bits(swiglu_oai(acc[t][tt][i], acc[t + 2][tt][i], g.alpha,
+                                                 g.limit));
+          amax = max(amax, hb[t][i] & 0x7FFFu);
+        }
+      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
+      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+      const uint32_t sbyte = mx8_scale_byte(amax);
+      const float inv = mx8_inv_scale(sbyte);
+      if (m >= g.live || !cols_live) continue;
+      const size_t r = (size_t)(g.row0 + g.p0 + m);
+      uint8_t* qrow = reinterpret_cast<uint8_t*>(g.out) + r * g.F + jb;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        uint32_t pk = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk |= e4m3_rne_sat(bf16_bits_to_f32(hb[t][i]) * inv) << (8 * i);
+        *reinterpret_cast<uint32_t*>(qrow + 16 * t + 4 * lg) = pk;
+      }
+      if (lg == 0) {
+        uint8_t* srow = g.out_scale + r * g.spo;
+        srow[blk] = (uint8_t)sbyte;
+        if (blk == nblk - 1)
+          for (int p = nblk; p < g.spo; ++p) srow[p] = 0;   // the row's padding
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) {
     const int m = tt * 16 + lr;
@@ -338,8 +385,8 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
 constexpr int kMxWaves = 4;
 constexpr int kMxThreads = 64 * kMxWaves;
 constexpr int kMxSC = 4;   // chunks per activation super-chunk
-__host__ __device__ constexpr int mx_wt(int act) { return act == MOE_ACT_SWIGLU_OAI ? 4 : 6; }
-__host__ __device__ constexpr int mx_wring(int act) { return act == MOE_ACT_SWIGLU_OAI ? 8 : 4; }
+__host__ __device__ constexpr int mx_wt(int act) { return act != MOE_ACT_NONE ? 4 : 6; }
+__host__ __device__ constexpr int mx_wring(int act) { return act != MOE_ACT_NONE ? 8 : 4; }
 constexpr int SRING_MAX = 2;   // scale groups in flight, at most (mx_wring / kMxSC)
 static_assert(gemm_dummy_off(true) == 2 * kMxSC * gemm_buf_bytes(kGmTT, true), "MX LDS layout");
 
@@ -539,8 +586,8 @@ gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int
             const int32_t* __restrict__ a_row, const uint8_t* __restrict__ q,
             const uint8_t* __restrict__ s, const float* __restrict__ bias,
             const int32_t* __restrict__ counts, const int32_t* __restrict__ basep, int E, int N,
-            int K, float alpha, float limit, void* __restrict__ out, int nbx, int nslots,
-            int per_xcd) {
+            int K, float alpha, float limit, void* __restrict__ out,
+            uint8_t* __restrict__ out_scale, int nbx, int nslots, int per_xcd) {
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   // XCD-aware tile order: the hardware deals workgroup ids to the 8 XCDs round robin, so id L
   // runs on XCD L % 8; virtual tile v = (L % 8) * per_xcd + L / 8 gives every XCD a contiguous
@@ -553,12 +600,14 @@ gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int
   const int c64 = ((int)(threadIdx.x & 63) < E) ? counts[threadIdx.x & 63] : 0;
   const int e = wave_slot_expert(counts, E, slot, c64);
   if (e < 0) return;   // uniform over the workgroup: fewer live experts than slots
-  constexpr bool swiglu = (ACT == MOE_ACT_SWIGLU_OAI);
+  constexpr bool swiglu = (ACT != MOE_ACT_NONE);
   GemmCtx g;
   g.a_row = a_row;
   g.bias = bias;
   g.out = out;
   g.a_scale = a_scale;
+  g.out_scale = out_scale;
+  g.spo = scale_row_bytes((N >> 1) >> 5);
   g.e = e;
   g.N = N;
   g.K = K;
@@ -652,15 +701,15 @@ template <bool MX8>
 int gemm_launch(const void* a, const uint8_t* a_scale, const int32_t* a_row, int64_t a_rows,
                 const mx4_experts* w, const int32_t* counts, const int32_t* basep, int tile_m,
                 int64_t mpad_max, int act, float alpha, float limit, void* out,
-                hipStream_t stream) {
+                uint8_t* out_scale, hipStream_t stream) {
   // buffer resources address at most 2 GB: one expert's weights and the activation matrix
   if ((int64_t)w->N * w->K / 2 >= (1LL << 31) ||
       a_rows * w->K * (MX8 ? 1 : 2) >= (1LL << 31) ||
       a_rows * scale_row_bytes(w->K / 32) >= (1LL << 31))
     return MOE_ESHAPE;
   const int64_t rows_per_wg = 16 * kGmWaves * gemm_wt(MOE_ACT_NONE);
-  const int64_t bx = (act == MOE_ACT_SWIGLU_OAI) ? (w->N / 2 + 127) / 128
-                                                 : (w->N + rows_per_wg - 1) / rows_per_wg;
+  const int64_t bx = (act != MOE_ACT_NONE) ? (w->N / 2 + 127) / 128
+                                            : (w->N + rows_per_wg - 1) / rows_per_wg;
   int64_t slots = mpad_max / tile_m;
   if (slots > w->E) slots = w->E;
   // > 64 KB of dynamic LDS must be opted into, once per kernel, at the largest size used
@@ -670,6 +719,10 @@ int gemm_launch(const void* a, const uint8_t* a_scale, const int32_t* a_row, int
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MOE_ACT_NONE, MX8>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_max) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MOE_ACT_SWIGLU_OAI, MX8>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds_max) != hipSuccess)
+      return MOE_ELAUNCH;
+    if (MX8 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MOE_ACT_SWIGLU_OAI_MX8, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_max) != hipSuccess)
       return MOE_ELAUNCH;
     lds_attr_set = true;
@@ -682,11 +735,17 @@ int gemm_launch(const void* a, const uint8_t* a_scale, const int32_t* a_row, int
   if (act == MOE_ACT_SWIGLU_OAI)
     launch(gemm_kernel<MOE_ACT_SWIGLU_OAI, MX8>, grid, block, lds, stream, a, a_scale,
            (int)a_rows, a_row, w->q, w->s, w->bias, counts, basep, w->E, w->N, w->K, alpha,
-           limit, out, (int)bx, (int)slots, (int)per_xcd);
-  else
+           limit, out, out_scale, (int)bx, (int)slots, (int)per_xcd);
+  else if (act == MOE_ACT_NONE)
     launch(gemm_kernel<MOE_ACT_NONE, MX8>, grid, block, lds, stream, a, a_scale, (int)a_rows,
            a_row, w->q, w->s, w->bias, counts, basep, w->E, w->N, w->K, alpha, limit, out,
-           (int)bx, (int)slots, (int)per_xcd);
+           out_scale, (int)bx, (int)slots, (int)per_xcd);
+  else if constexpr (MX8)
+    launch(gemm_kernel<MOE_ACT_SWIGLU_OAI_MX8, true>, grid, block, lds, stream, a, a_scale,
+           (int)a_rows, a_row, w->q, w->s, w->bias, counts, basep, w->E, w->N, w->K, alpha,
+           limit, out, out_scale, (int)bx, (int)slots, (int)per_xcd);
+  else
+    return MOE_EINVAL;
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
@@ -696,13 +755,13 @@ int moe_launch_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, con
                     const int32_t* counts, const int32_t* basep, int tile_m, int64_t mpad_max,
                     int act, float alpha, float limit, void* out, hipStream_t stream) {
   return moe::gemm_launch<false>(a, nullptr, a_row, a_rows, w, counts, basep, tile_m, mpad_max,
-                                 act, alpha, limit, out, stream);
+                                 act, alpha, limit, out, nullptr, stream);
 }
 
 int moe_launch_gemm_mx8(const uint8_t* aq, const uint8_t* as, const int32_t* a_row,
                         int64_t a_rows, const mx4_experts* w, const int32_t* counts,
                         const int32_t* basep, int tile_m, int64_t mpad_max, int act, float alpha,
-                        float limit, void* out, hipStream_t stream) {
+                        float limit, void* out, uint8_t* out_scale, hipStream_t stream) {
   return moe::gemm_launch<true>(aq, as, a_row, a_rows, w, counts, basep, tile_m, mpad_max, act,
-                                alpha, limit, out, stream);
+                                alpha, limit, out, out_scale, stream);
 }

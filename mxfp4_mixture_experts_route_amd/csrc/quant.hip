@@ -17,26 +17,6 @@
 
 namespace moe {
 
-// E4M3 byte of a finite fp32 value t with |t| < 2^9, round to nearest even, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float t) {
-  const uint32_t u = __float_as_uint(t);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t mag;
-  if (a < 0x3C800000u) {                      // |t| < 2^-6: subnormal step 2^-9
-    // |t| * 2^9 < 8 is exact; rintf rounds half to even; 8 lands on 2^-6 = byte 0x08
-    mag = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
-  } else {
-    // keep 3 mantissa bits, rounding half to even (a carry into the exponent is a correct
-    // round up to the next binade)
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    const int ex = (int)(r >> 23) - 127;      // >= -6
-    const uint32_t m3 = (r >> 20) & 7u;
-    mag = (ex > 8 || (ex == 8 && m3 == 7u)) ? 0x7Eu : ((uint32_t)(ex + 7) << 3) | m3;
-  }
-  return sign | mag;
-}
-
 // Four lanes per 32-value block, 8 values (16 bytes) each: a wavefront covers 16 consecutive
 // blocks, i.e. 1 KB of bf16 read and 512 bytes of E4M3 written, contiguous across its lanes.
 __global__ void __launch_bounds__(256)
@@ -66,9 +46,8 @@ mx8_quantize_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ 
   if (!active) return;
   // exponent field Ea of the largest magnitude: floor(log2 m) = Ea - 127 for a normal m, so
   // the scale byte X + 127 = Ea - 8, clamped at 0 (a zero or subnormal m has Ea = 0)
-  const int ea = (int)(amax >> 7);
-  const uint32_t sbyte = (uint32_t)max(ea - 8, 0);
-  const float inv = __uint_as_float((254u - sbyte) << 23);   // 2^(127 - sbyte) = 2^-X, exact
+  const uint32_t sbyte = mx8_scale_byte(amax);
+  const float inv = mx8_inv_scale(sbyte);   // 2^(127 - sbyte) = 2^-X, exact
   uint32_t out[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {

@@ -192,9 +192,9 @@ def test_gemm_mx8_argument_checks():
     NONE, SW = _lib.MOE_ACT_NONE, _lib.MOE_ACT_SWIGLU_OAI
 
     def call(aq=FAKE, as_=FAKE, a_row=FAKE, a_rows=8, w=good, counts=FAKE, basep=FAKE,
-             tile_m=16, mpad=64, act=NONE, out=FAKE):
+             tile_m=16, mpad=64, act=NONE, out=FAKE, out_scale=None):
         return f(aq, as_, a_row, a_rows, None if w is None else ctypes.byref(w), counts, basep,
-                 tile_m, mpad, act, 1.702, 7.0, out, None)
+                 tile_m, mpad, act, 1.702, 7.0, out, out_scale, None)
 
     assert call(aq=None) == _lib.MOE_EINVAL
     assert call(as_=None) == _lib.MOE_EINVAL
@@ -209,6 +209,11 @@ def test_gemm_mx8_argument_checks():
     assert call(aq=ctypes.c_void_p(0x1008)) == _lib.MOE_EALIGN
     assert call(as_=ctypes.c_void_p(0x1008)) == _lib.MOE_EALIGN
     assert call(out=ctypes.c_void_p(0x1002)) == _lib.MOE_EALIGN
+    Q = _lib.MOE_ACT_SWIGLU_OAI_MX8
+    assert call(act=Q) == _lib.MOE_EINVAL                                 # out_scale missing
+    assert call(act=Q, out_scale=FAKE, w=experts(N=96)) == _lib.MOE_ESHAPE  # N % 64
+    assert call(act=Q, out_scale=ctypes.c_void_p(0x1004)) == _lib.MOE_EALIGN
+    assert call(act=3) == _lib.MOE_EINVAL
 
 
 @no_gpu

@@ -86,6 +86,10 @@ def test_quantize_skips_rows_that_are_not_live():
 
 
 def gemm8(aq, as_, a_row, W, counts, basep, tile_m, mpad, act, out=None):
+    if act == moe.MOE_ACT_SWIGLU_OAI_MX8:
+        q, s = out if out is not None else (None, None)
+        return moe.mx4_moe_gemm_mx8(aq, as_, a_row, W, counts, basep, tile_m, mpad, act, ALPHA,
+                                    LIMIT, out=q, out_scale=s)
     return moe.mx4_moe_gemm_mx8(aq, as_, a_row, W, counts, basep, tile_m, mpad, act, ALPHA, LIMIT,
                                 out=out)
 
@@ -121,6 +125,19 @@ def staged_mx8(c):
     hq, hs = moe.mx8_quantize(h, live=row_tok)
     hq_h, hs_h = host(hq), host(hs)
     assert_quant_equal(hq_h[live], hs_h[live], h_bits[live], "h")
+
+    # the fused epilogue writes the same MXFP8 rows (h rounded to bf16 in-register, then the
+    # same conversion); rows that are not live stay untouched
+    if F % 32 == 0:
+        import torch
+        q2 = torch.full((mpad, F), 0xAB, dtype=torch.uint8, device="cuda")
+        s2 = torch.full((mpad, moe.scale_row_bytes(F)), 0xCD, dtype=torch.uint8, device="cuda")
+        gemm8(xq, xs, row_tok, GU, counts, basep, tile_m, mpad, moe.MOE_ACT_SWIGLU_OAI_MX8,
+              out=(q2, s2))
+        q2h, s2h = host(q2), host(s2)
+        assert np.array_equal(q2h[live], hq_h[live]) and np.array_equal(s2h[live], hs_h[live]), \
+            "fused MXFP8 h"
+        assert np.all(q2h[~live] == 0xAB) and np.all(s2h[~live] == 0xCD)
 
     d = host(gemm8(hq, hs, None, DN, counts, basep, tile_m, mpad, NONE,
                    out=sentinel_out(mpad, D, NONE)))
@@ -295,8 +312,10 @@ def test_full_size_layer_mx8(name):
     ref, S = oracle.project_mx8_at(xq_h, xs_h, rt_h, W["gate_up"]["q"], W["gate_up"]["s"],
                                    W["gate_up"]["bias"], cnt_h, bp_h, list(zip(rows, cols)))
     assert_within(g[rows, cols], ref, S, f"{name} gate_up mx8")
-    # SwiGLU from the GPU's own g
-    h_bits = bf16_host(out["h"])
+    # SwiGLU from the GPU's own g (the bf16 epilogue of the same call)
+    h_bits = bf16_host(moe.mx4_moe_gemm_mx8(out["xq"], out["xs"], out["row_tok"], GU,
+                                            out["counts"], out["basep"], wl.tile_m, mpad, SWIGLU,
+                                            ALPHA, LIMIT))
     js = rng.integers(0, wl.ffn, N_SAMPLES)
     pair = np.stack([g[rows, js], g[rows, wl.ffn + js]], axis=1)
     assert_bf16_within_ulp(h_bits[rows, js],

@@ -289,6 +289,14 @@ EDGE = {
     "counts_around_granules": dict(seed=5, E=6, D=64, F=64, T=456, k=1, tile_m=16,
                                    ids=skewed_ids([15, 16, 17, 135, 136, 137], 5)),
     "tile_m_7": dict(seed=6, E=5, D=96, F=64, T=33, k=3, tile_m=7),
+    # tall passes: 256 rows = two full 128-row passes; 320 = two plus a 64-row remainder pass;
+    # 136 rows on one expert beside a 32-row one (a full pass plus an 8-row remainder)
+    "m256_one_expert": dict(seed=8, E=3, D=64, F=64, T=256, k=1, tile_m=16,
+                            ids=np.full((256, 1), 1, dtype=np.int32)),
+    "m320_one_expert": dict(seed=9, E=3, D=96, F=64, T=320, k=1, tile_m=16,
+                            ids=np.full((320, 1), 2, dtype=np.int32)),
+    "m136_and_32": dict(seed=10, E=4, D=64, F=96, T=168, k=1, tile_m=16,
+                        ids=skewed_ids([0, 136, 0, 32], 10)),
     "tile_m_32": dict(seed=7, E=16, D=64, F=96, T=70, k=4, tile_m=32),
 }
 
