@@ -143,8 +143,12 @@ int moe_bucket(const int32_t* ids, int64_t T, int k, int E, int tile_m, int64_t 
  *       16 * (e*N*KB + (kb/4)*N*4 + n*w_c + (kb%4)). Same size as the checkpoint's q. Every
  *       16 consecutive rows of a chunk are one contiguous run of 16*w_c*16 bytes, which is what
  *       one wavefront of the projection kernels reads per load instruction.
- *     scales: row-major with every row padded to SP = roundup(KB, 16) bytes (padding bytes 0):
- *       the scale of block (e, n, kb) is byte (e*N + n)*SP + kb. Size E*N*SP bytes.
+ *     scales: each row's KB scale bytes are cut into G = ceil(KB/16) groups of 16 (the scales
+ *       of 4 chunks), stored group after group with all N rows of a group together: the scale
+ *       of block (e, n, kb) is byte 16 * ((e*G + kb/16)*N + n) + kb%16, and the bytes past KB
+ *       in the last group are 0. Size E*N*SP bytes, SP = 16*G = roundup(KB, 16). Every 16
+ *       consecutive rows of a group are one contiguous 256-byte run, which one wavefront reads
+ *       with one load.
  * mx4_experts describes a stack in the CHUNKED layout. The descriptor itself is a HOST struct;
  * q, s and bias are device pointers; bias is f32 [E][N] or NULL.
  */
@@ -159,7 +163,7 @@ typedef struct {
 
 /*
  * Repack an expert stack from the checkpoint layout to the chunked layout (a byte permutation
- * plus the scale-row padding, run once when the weights are loaded). q_src/s_src in the
+ * plus the zero padding of the last scale group, run once when the weights are loaded). q_src/s_src in the
  * checkpoint layout (E*N*K/2 and E*N*K/32 bytes); q_dst (E*N*K/2 bytes) and s_dst
  * (E*N*roundup(K/32, 16) bytes) receive the chunked layout; no buffer may overlap another.
  * Errors: MOE_EINVAL for NULL pointers or E/N < 1; MOE_ESHAPE for K < 32 or K % 32 != 0;

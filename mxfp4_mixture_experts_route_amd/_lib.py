@@ -153,7 +153,7 @@ class MX4Experts:
             if tuple(bias.shape) != (E, N):
                 raise ValueError(f"bias: expected shape {(E, N)}")
         qp = torch.empty_like(q)
-        sp = torch.empty((E, N, scale_row_bytes(K)), dtype=torch.uint8, device=q.device)
+        sp = torch.empty((E, scale_row_bytes(K) // 16, N, 16), dtype=torch.uint8, device=q.device)
         _call("mx4_pack_experts", _ptr(q), _ptr(s), E, N, K, _ptr(qp), _ptr(sp), _stream(stream))
         self.q, self.s, self.bias = qp, sp, bias
         self.E, self.N, self.K = E, N, K
@@ -180,19 +180,22 @@ def np_contig(a):
 
 
 def scale_row_bytes(K: int) -> int:
-    """Bytes per scale row in the chunked layout: K/32 padded to a multiple of 16."""
+    """K/32 padded to a multiple of 16: the scale bytes per row of the chunked layout (in
+    groups of 16) and the pitch of MXFP8 scale rows."""
     return (K // 32 + 15) // 16 * 16
 
 
 def mx4_pack_experts(q, s, q_dst=None, s_dst=None, stream=None):
-    """Checkpoint-layout MXFP4 stack -> chunked layout: q_dst like q, s_dst u8 [E][N][SP]."""
+    """Checkpoint-layout MXFP4 stack -> chunked layout: q_dst like q, s_dst u8 [E][SP/16][N][16]
+    (scale groups of 16 blocks, all rows of a group together)."""
     torch = _torch()
     _check(q, torch.uint8, "q")
     _check(s, torch.uint8, "s")
     E, N, half_k = q.shape
     q_dst = torch.empty_like(q) if q_dst is None else q_dst
     if s_dst is None:
-        s_dst = torch.empty((E, N, scale_row_bytes(half_k * 2)), dtype=torch.uint8, device=q.device)
+        s_dst = torch.empty((E, scale_row_bytes(half_k * 2) // 16, N, 16), dtype=torch.uint8,
+                            device=q.device)
     _call("mx4_pack_experts", _ptr(q), _ptr(s), E, N, half_k * 2, _ptr(q_dst), _ptr(s_dst),
           _stream(stream))
     return q_dst, s_dst

@@ -89,8 +89,14 @@ __host__ __device__ constexpr int gemm_dummy_off(bool mx8) {
 }
 // LDS pitch of a staged scale row: fixed, so that a token tile's offset is an immediate
 constexpr int kGmScalePitch = MOE_MX8_GEMM_MAX_K / 32;
+constexpr int kMxWaves = 8;              // MXFP8 variant: 2 wavefronts per SIMD as well
+// MXFP8 passes, after the staged scale rows: the per-wavefront h block maxima that the MXFP8
+// epilogue exchanges (one word per wavefront and routed row)
+__host__ __device__ constexpr int gemm_amax_off() {
+  return gemm_dummy_off(true) + 1024 + kGmTT * 16 * kGmScalePitch;
+}
 __host__ __device__ constexpr int gemm_lds_bytes(bool mx8) {
-  return gemm_dummy_off(mx8) + 1024 + (mx8 ? kGmTT * 16 * kGmScalePitch : 0);
+  return mx8 ? gemm_amax_off() + kMxWaves * kGmTT * 16 * 4 : gemm_dummy_off(false) + 1024;
 }
 // 16-byte piece q of routed row m of an MXFP8 chunk sits at slot q ^ gemm_swz8(m) of the row's
 // 128 bytes: the B-fragment reads of 16 consecutive rows at one q then touch 16 different
@@ -103,6 +109,7 @@ struct GemmCtx {
   const float* bias;
   void* out;
   const uint8_t* a_scale;   // MXFP8 activation scale rows (pitch spa), else unused
+  uint8_t* xs;              // the workgroup's LDS
   uint8_t* out_scale;       // MOE_ACT_SWIGLU_OAI_MX8: e8m0 rows of h (pitch spo)
   int spo;
   __amdgpu_buffer_rsrc_t rq, rs, ra, ras;
@@ -112,7 +119,7 @@ struct GemmCtx {
   int tile_base[kGmMaxWT];
   int rows_in[kGmMaxWT];
   uint32_t wo[kGmMaxWT], wol[kGmMaxWT], so[kGmMaxWT];
-  uint32_t sg[kGmMaxWT];   // the lane's scale row (16-byte groups of 4 chunks)
+  uint32_t sg[kGmMaxWT];   // the lane's row in a scale group (16 bytes: 4 chunks)
 };
 
 // Epilogue of a pass: lane holds rows 4*lg..4*lg+3 of each weight tile for token column lr.
@@ -123,42 +130,51 @@ __device__ __forceinline__ void gemm_epilogue(const GemmCtx& g, const f32x4_t (&
   constexpr int kGmWT = WT;
   const int lr = g.lr, lg = g.lg;
   if constexpr (ACT == MOE_ACT_SWIGLU_OAI_MX8) {
-    // MXFP8 rows of h: with 4 tiles per wavefront its 32 h columns [jb, jb + 32) (gate tiles 0
-    // and 1, up tiles 2 and 3) are one MX block per token row, held by the 4 lanes of a token
-    // column (lg = 0..3, 8 values each): the block maximum takes two cross-lane steps. Values
-    // are the bf16-rounded SwiGLU-OAI outputs, scaled and encoded as mx8_quantize does.
-    static_assert(WT == 4, "one 32-column block per wavefront");
+    // MXFP8 rows of h. A wavefront holds 16 h columns [jb, jb + 16) (gate tile 0, up tile 1),
+    // rows 4*lg..4*lg+3 of them per lane; an MX block of 32 columns is the work of wavefronts
+    // 2i and 2i + 1. The block maximum per token row: over the lane's 4 values, the 4 lanes of
+    // the token column (two cross-lane steps), then the partner wavefront's maximum through LDS.
+    // Values are the bf16-rounded SwiGLU-OAI outputs, scaled and encoded as mx8_quantize does.
+    static_assert(WT == 2, "16 columns per wavefront, a block per wavefront pair");
     const int jb = g.tile_base[0];
-    const bool cols_live = jb < g.F;                 // F % 32 == 0: the block is whole or absent
+    const bool cols_live = jb < g.F;   // F % 32 == 0: both halves of the block exist or neither
     const int blk = jb >> 5, nblk = g.F >> 5;
+    const int wave = g.tid >> 6;
+    uint32_t* const amax_w = reinterpret_cast<uint32_t*>(g.xs + gemm_amax_off());
+    uint32_t hp[NTT][2];   // the lane's 4 bf16 values, two per word
+    uint32_t amax[NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      uint32_t a = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t hb =
+            f32_to_bf16_bits(swiglu_oai(acc[0][tt][i], acc[1][tt][i], g.alpha, g.limit));
+        a = max(a, hb & 0x7FFFu);
+        if (i % 2 == 0) hp[tt][i / 2] = hb;
+        else hp[tt][i / 2] |= hb << 16;
+      }
+      a = max(a, (uint32_t)__shfl_xor((int)a, 16));
+      a = max(a, (uint32_t)__shfl_xor((int)a, 32));
+      amax[tt] = a;
+      if (lg == 0) amax_w[wave * (kGmTT * 16) + tt * 16 + lr] = a;
+    }
+    __syncthreads();
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
       const int m = tt * 16 + lr;
-      uint32_t hb[2][4];
-      uint32_t amax = 0;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hb[t][i] = f32_to_bf16_bits(swiglu_oai(acc[t][tt][i], acc[t + 2][tt][i], g.alpha,
-                                                 g.limit));
-          amax = max(amax, hb[t][i] & 0x7FFFu);
-        }
-      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
-      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
-      const uint32_t sbyte = mx8_scale_byte(amax);
+      const uint32_t a = max(amax[tt], amax_w[(wave ^ 1) * (kGmTT * 16) + m]);
+      const uint32_t sbyte = mx8_scale_byte(a);
       const float inv = mx8_inv_scale(sbyte);
       if (m >= g.live || !cols_live) continue;
       const size_t r = (size_t)(g.row0 + g.p0 + m);
-      uint8_t* qrow = reinterpret_cast<uint8_t*>(g.out) + r * g.F + jb;
+      uint32_t pk = 0;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        uint32_t pk = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk |= e4m3_rne_sat(bf16_bits_to_f32(hb[t][i]) * inv) << (8 * i);
-        *reinterpret_cast<uint32_t*>(qrow + 16 * t + 4 * lg) = pk;
-      }
-      if (lg == 0) {
+      for (int i = 0; i < 4; ++i)
+        pk |= e4m3_rne_sat(bf16_bits_to_f32((hp[tt][i / 2] >> (16 * (i % 2))) & 0xFFFFu) * inv)
+              << (8 * i);
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(g.out) + r * g.F + jb + 4 * lg) = pk;
+      if (lg == 0 && (wave & 1) == 0) {
         uint8_t* srow = g.out_scale + r * g.spo;
         srow[blk] = (uint8_t)sbyte;
         if (blk == nblk - 1)
@@ -234,7 +250,8 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
     const int cc = min(c, C - 1);
     const bool last = cc == C - 1;
     const uint32_t cq = (uint32_t)cc * g.N * (kChunkBlocks * 16);
-    const uint32_t cs = (uint32_t)cc * kChunkBlocks;   // scale byte of block 4c + lg
+    // scale byte of block 4c + lg: byte 4 (c % 4) + lg of the row's 16 bytes in group c / 4
+    const uint32_t cs = (uint32_t)(cc >> 2) * g.N * 16 + (uint32_t)(cc & 3) * kChunkBlocks;
 #pragma unroll
     for (int t = 0; t < kGmWT; ++t) {
       dq[t] = buf_load16(g.rq, last ? g.wol[t] : g.wo[t], cq);
@@ -382,10 +399,9 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
 //    complete in issue order); the barrier makes it every wavefront's and frees the half that
 //    the next DMA overwrites. The weights of each chunk are waited for by the compiler
 //    (register dependencies).
-constexpr int kMxWaves = 4;
 constexpr int kMxThreads = 64 * kMxWaves;
 constexpr int kMxSC = 4;   // chunks per activation super-chunk
-__host__ __device__ constexpr int mx_wt(int act) { return act != MOE_ACT_NONE ? 4 : 6; }
+__host__ __device__ constexpr int mx_wt(int act) { return act != MOE_ACT_NONE ? 2 : 3; }
 __host__ __device__ constexpr int mx_wring(int act) { return act != MOE_ACT_NONE ? 8 : 4; }
 constexpr int SRING_MAX = 2;   // scale groups in flight, at most (mx_wring / kMxSC)
 static_assert(gemm_dummy_off(true) == 2 * kMxSC * gemm_buf_bytes(kGmTT, true), "MX LDS layout");
@@ -422,7 +438,7 @@ __device__ __forceinline__ void gemm_pass_mx8(const GemmCtx& g, uint8_t* __restr
   static_assert(SC == 4, "a 16-byte scale load covers 4 chunks");
   const int S_last = (C - 1) / SC;
   auto load_s = [&](int s, u32x4_t (&ds)[WT]) {
-    const uint32_t off = (uint32_t)min(s, S_last) * 16;
+    const uint32_t off = (uint32_t)min(s, S_last) * g.N * 16;
 #pragma unroll
     for (int t = 0; t < WT; ++t) ds[t] = buf_load16(g.rs, g.sg[t], off);
   };
@@ -539,7 +555,8 @@ __device__ __forceinline__ void gemm_pass_mx8(const GemmCtx& g, uint8_t* __restr
           auto read_b = [&](int tt, i32x8_t& B, int& sb) {
             const u32x4_t b0 = *reinterpret_cast<const u32x4_t*>(xb0 + tt * 16 * ROWB);
             const u32x4_t b1 = *reinterpret_cast<const u32x4_t*>(xb1 + tt * 16 * ROWB);
-            sb = kb_live ? (int)sbp[tt * 16 * kGmScalePitch] : 0;
+            const int sv = sbp[tt * 16 * kGmScalePitch];   // read always, then select: no branch
+            sb = kb_live ? sv : 0;
             B = i32x8_t{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
                         (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
           };
@@ -558,7 +575,7 @@ __device__ __forceinline__ void gemm_pass_mx8(const GemmCtx& g, uint8_t* __restr
               acc[t][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                   A, B, acc[t][tt], kMfmaFmtFp4, kMfmaFmtFp8, 0, sa[t], 0, sb);
             }
-            __builtin_amdgcn_sched_barrier(0);
+            issue_fence();   // B of token tile tt + 1 only: LDS reads stay one tile ahead
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -607,6 +624,7 @@ gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int
   g.out = out;
   g.a_scale = a_scale;
   g.out_scale = out_scale;
+  g.xs = xs;
   g.spo = scale_row_bytes((N >> 1) >> 5);
   g.e = e;
   g.N = N;
@@ -651,7 +669,7 @@ gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int
   const int SP = scale_row_bytes(KB);        // scale row pitch (padding reads as 0)
   g.spa = SP;                                // MXFP8 activation scale rows use the same pitch
   g.rq = make_rsrc(q + 16 * ebase, (uint32_t)N * KB * 16);
-  g.rs = make_rsrc(s + (size_t)e * N * SP, (uint32_t)N * SP);
+  g.rs = make_rsrc(s + (size_t)e * N * SP, (uint32_t)N * SP);   // SP / 16 groups of N rows
   g.ra = make_rsrc(a, (uint32_t)a_rows * K * (MX8 ? 1 : 2));
   g.ras = make_rsrc(a_scale, MX8 ? (uint32_t)a_rows * SP : 0u);
 
@@ -660,8 +678,8 @@ gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int
   for (int t = 0; t < kGmWT; ++t) {
     const uint32_t n = (uint32_t)(g.tile_base[t] + g.lr);
     const bool ok = g.lr < g.rows_in[t];
-    g.so[t] = ok ? n * SP + g.lg : kOOB;
-    g.sg[t] = ok ? n * SP : kOOB;
+    g.so[t] = ok ? n * 16 + g.lg : kOOB;   // the row's 16 bytes in a scale group
+    g.sg[t] = ok ? n * 16 : kOOB;
     g.wo[t] = ok ? (n * kChunkBlocks + g.lg) * 16 : kOOB;
     g.wol[t] = (ok && g.lg < wlast) ? (n * wlast + g.lg) * 16 : kOOB;
   }

@@ -82,7 +82,7 @@ template <int SEG>
 struct Mx4Wave {
   __amdgpu_buffer_rsrc_t rq, rs;
   uint32_t wo, wol, so;
-  int C, ce, SP, N, lg;
+  int C, ce, G, N, lg;
   u32x4_t wq[SEG];
   uint32_t sc[SEG];
 
@@ -96,24 +96,24 @@ struct Mx4Wave {
     const int KB = K >> 5;
     C = (KB + kChunkBlocks - 1) / kChunkBlocks;
     ce = ce_;
-    SP = scale_row_bytes(KB);
+    G = scale_row_bytes(KB) / 16;
     const int wlast = KB - (C - 1) * kChunkBlocks;
     rq = make_rsrc(q + 16 * (size_t)e * N * KB, (uint32_t)N * KB * 16);
-    rs = make_rsrc(s + (size_t)e * N * SP, (uint32_t)N * SP);
+    rs = make_rsrc(s + (size_t)e * N * G * 16, (uint32_t)N * G * 16);
     wo = valid ? ((uint32_t)n * kChunkBlocks + lg) * 16 : kOOB;                // full chunk
     wol = (valid && lg < wlast) ? ((uint32_t)n * wlast + lg) * 16 : kOOB;      // last chunk
-    so = valid ? (uint32_t)n * SP : kOOB;
+    so = valid ? (uint32_t)n * 16 : kOOB;   // the row's 16 bytes in a scale group
   }
 
   // Chunks [c0, c0 + SEG): scales and nibbles, in K order. A chunk past K or past ce reads
-  // zeros (branch-free); a scale group past the padded scale row reads zeros (it would
-  // otherwise read the next row's scales, where a NaN byte would poison 0 * scale). The
+  // zeros (branch-free); a scale group past the last one reads zeros (it would otherwise read
+  // another expert's scales, where a NaN byte would poison 0 * scale). The
   // scheduling barriers keep the issue order (the compiler would move the scale loads last).
   __device__ __forceinline__ void load_segment(int c0) {
 #pragma unroll
     for (int i = 0; i < SEG / 4; ++i) {
-      const uint32_t g_off = (uint32_t)(c0 + 4 * i) * 4;
-      const u32x4_t v = buf_load16(rs, g_off < (uint32_t)SP ? so : kOOB, g_off);
+      const int gi = (c0 + 4 * i) / 4;   // c0 is a multiple of 4: whole groups
+      const u32x4_t v = buf_load16(rs, gi < G ? so : kOOB, (uint32_t)gi * N * 16);
       sc[4 * i + 0] = v[0];
       sc[4 * i + 1] = v[1];
       sc[4 * i + 2] = v[2];

@@ -2,7 +2,7 @@
 //
 // A pure byte permutation, run once when weights are loaded: one thread per 16-byte MX block,
 // reading the source in order (coalesced) and writing the block to its chunked position and its
-// scale byte to the padded scale row. The chunked layout makes each wavefront load of the projection kernels one
+// scale byte to its scale group (16 blocks of one row; all rows of a group together). The chunked layout makes each wavefront load of the projection kernels one
 // contiguous 1 KB run and keeps all workgroups of a launch inside a compact window of memory.
 #include "common.hpp"
 #include "launch.hpp"
@@ -15,7 +15,7 @@ __global__ void __launch_bounds__(kPackThreads)
 pack_kernel(const uint8_t* __restrict__ q_src, const uint8_t* __restrict__ s_src, int E, int N,
             int KB, uint8_t* __restrict__ q_dst, uint8_t* __restrict__ s_dst) {
   const size_t total = (size_t)E * N * KB;
-  const int SP = scale_row_bytes(KB);
+  const int G = scale_row_bytes(KB) / 16;   // scale groups per row
   for (size_t i = (size_t)blockIdx.x * kPackThreads + threadIdx.x; i < total;
        i += (size_t)gridDim.x * kPackThreads) {
     const int kb = (int)(i % KB);
@@ -24,10 +24,10 @@ pack_kernel(const uint8_t* __restrict__ q_src, const uint8_t* __restrict__ s_src
     const int e = (int)(row / N);
     const size_t d = chunked_block(e, n, kb, N, KB);
     *reinterpret_cast<uint4*>(q_dst + 16 * d) = *reinterpret_cast<const uint4*>(q_src + 16 * i);
-    uint8_t* srow = s_dst + row * SP;
-    srow[kb] = s_src[i];
+    uint8_t* grp = s_dst + 16 * (((size_t)e * G + kb / 16) * N + n);
+    grp[kb % 16] = s_src[i];
     if (kb == KB - 1)
-      for (int p = KB; p < SP; ++p) srow[p] = 0;   // padding of the scale row
+      for (int p = kb % 16 + 1; p < 16; ++p) grp[p] = 0;   // padding of the last group
   }
 }
 

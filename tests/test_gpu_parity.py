@@ -69,8 +69,8 @@ MEDIUM = dict(seed=11, E=8, D=320, F=224, T=100, k=4, tile_m=16)
 
 def chunked_reference(q, s):
     """The chunked layout written out with numpy: nibbles per expert chunk by chunk (blocks
-    4c .. 4c+w_c-1 of all N rows, row after row); scales row-major, each row zero-padded to a
-    multiple of 16 bytes."""
+    4c .. 4c+w_c-1 of all N rows, row after row); scales per expert in groups of 16 blocks, all
+    N rows of a group together (16 bytes each), the last group zero-padded."""
     E, N, half_k = q.shape
     KB = half_k // 16
     qb = q.reshape(E, N, KB, 16)
@@ -80,9 +80,10 @@ def chunked_reference(q, s):
             w = min(4, KB - c0)
             qo.append(qb[e, :, c0:c0 + w, :].reshape(-1))
     SP = (KB + 15) // 16 * 16
-    so = np.zeros((E, N, SP), dtype=np.uint8)
-    so[:, :, :KB] = s
-    return np.concatenate(qo), so.reshape(-1)
+    rows = np.zeros((E, N, SP), dtype=np.uint8)
+    rows[:, :, :KB] = s
+    so = rows.reshape(E, N, SP // 16, 16).transpose(0, 2, 1, 3)   # [E][group][N][16]
+    return np.concatenate(qo), np.ascontiguousarray(so).reshape(-1)
 
 
 @pytest.mark.parametrize("E,N,K", [(3, 37, 160), (2, 16, 32), (4, 64, 2880), (1, 5, 96)])
