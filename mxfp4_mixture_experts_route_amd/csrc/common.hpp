@@ -134,14 +134,18 @@ __device__ __forceinline__ float mx8_inv_scale(uint32_t sbyte) {
 }
 
 // Clamped SwiGLU-OAI of one (gate, up) pair: gc = min(gate, limit), uc = clamp(up, +-limit),
-// gc * sigmoid(alpha*gc) * (uc + 1). The sigmoid is evaluated on the side where exp() cannot
-// overflow, so very negative gates give correctly tiny (not zero-by-overflow) results.
+// gc * sigmoid(alpha*gc) * (uc + 1). The sigmoid is evaluated on the side where the exponential
+// cannot overflow (e = exp(-|z|) <= 1), so very negative gates give correctly tiny (not
+// zero-by-overflow) results. exp(-|z|) = 2^(-|z| log2 e) and 1 / (1 + e) use the hardware's
+// exp2 and reciprocal (about 1 ulp each, far below the bf16 rounding of h); the accurate library
+// exp and IEEE division cost ~40 VALU ops per value in epilogues that run while HBM idles.
 __device__ __forceinline__ float swiglu_oai(float gate, float up, float alpha, float limit) {
-  float gc = fminf(gate, limit);
-  float uc = fminf(fmaxf(up, -limit), limit);
-  float z = alpha * gc;
-  float ez = expf(-fabsf(z));
-  float sig = (z >= 0.0f) ? 1.0f / (1.0f + ez) : ez / (1.0f + ez);
+  const float gc = fminf(gate, limit);
+  const float uc = fminf(fmaxf(up, -limit), limit);
+  const float z = alpha * gc;
+  const float ez = __builtin_amdgcn_exp2f(-fabsf(z) * 1.44269504088896341f);
+  const float r = __builtin_amdgcn_rcpf(1.0f + ez);
+  const float sig = (z >= 0.0f) ? r : ez * r;
   return gc * sig * (uc + 1.0f);
 }
 
