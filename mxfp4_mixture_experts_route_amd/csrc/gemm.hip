@@ -8,7 +8,7 @@
 // lab-winning shape" (the matmul's weight stage: 16-byte block loads, e2m1 table decode, e8m0
 // applied arithmetically).
 //
-// gfx950 mapping. One workgroup (4 wavefronts) owns one expert and one slice of weight rows and
+// gfx950 mapping. One workgroup (8 wavefronts) owns one expert and one slice of weight rows and
 // runs over all of that expert's routed rows, so every weight byte is fetched from HBM once.
 //  * Weights are in the chunked layout (chunks of 4 MX blocks, all rows of a chunk together):
 //    a wavefront's load of 16 rows x 4 blocks is one contiguous 1 KB run, and at any moment the
@@ -387,12 +387,13 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
 }
 
 // MXFP8 pass on the MX-scaled MFMA. The arithmetic per byte is small here (no decode, one MFMA
-// per 16x16x128 tile product), so the pass is bound by how many weight bytes are in flight: one
-// wavefront per SIMD (4 per workgroup) with its accumulators allowed into the AGPR half of the
-// register file, so each wavefront can hold a deep ring of weight chunks (SwiGLU: 8 chunks of 4
-// tiles, 32 KB; plain: 4 chunks of 6 tiles, 24 KB). The activations move in super-chunks of 4
-// chunks, double-buffered in LDS, so the workgroup meets at a barrier once per 4 chunks; between
-// barriers each wavefront streams its own weights.
+// per 16x16x128 tile product), so the pass is bound by keeping weight bytes in flight while the
+// matrix core works: 8 wavefronts, 2 per SIMD (one waits on memory while the other issues
+// MFMAs), each with a ring of weight chunks (SwiGLU: 8 chunks of 2 tiles, 16 KB; plain: 4 chunks
+// of 3 tiles, 12 KB). The activations move in super-chunks of 4 chunks, double-buffered in LDS,
+// so the workgroup meets at a barrier once per 4 chunks; between barriers each wavefront
+// streams its own weights. B operands are read from LDS one token tile ahead of their MFMAs
+// (all of a chunk's at once would hold 8 x 8 registers).
 //  * Issue order per super-chunk: the DMA of the next super-chunk, then after each chunk's MFMAs
 //    the weight chunk WRING ahead into the slot just used. At the top of super-chunk s, waiting
 //    until only the 4 weight chunks issued after its DMA are outstanding lands that DMA (loads
@@ -595,8 +596,7 @@ __device__ __forceinline__ void gemm_pass_mx8(const GemmCtx& g, uint8_t* __restr
 
 __host__ __device__ constexpr int gemm_threads(bool mx8) { return mx8 ? kMxThreads : kGmThreads; }
 
-// bf16: 8 wavefronts, 2 per SIMD (256 registers each); MXFP8: 4 wavefronts, 1 per SIMD, which
-// lets each use up to 512 registers (accumulators in AGPRs)
+// Both variants: 8 wavefronts, 2 per SIMD (256 registers each)
 template <int ACT, bool MX8>
 __global__ void __launch_bounds__(gemm_threads(MX8), 1)
 gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int a_rows,
