@@ -305,8 +305,8 @@ def counter_pass(moe, synth, torch):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the expert-parallel "
-              "multi-GPU path is not part of this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); expert parallelism "
+              "across GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
     import numpy as np  # noqa: F401
     import torch
