@@ -46,6 +46,9 @@ def parse_args():
     p.add_argument("--counter-pass", action="store_true",
                    help="run only what the hardware-counter passes measure: a plain copy kernel of "
                         "known size, then the fused decode of 8 layers twice (no timing, no JSON)")
+    p.add_argument("--counter-pass-prefill", action="store_true",
+                   help="the same for the pp512 expert GEMMs: the copy kernel, then the pp512 chain "
+                        "over its layers twice with bf16 and twice with MXFP8 activations")
     return p.parse_args()
 
 
@@ -288,11 +291,7 @@ def measured_traffic():
 def counter_pass(moe, synth, torch):
     """Workload of the rocprofv3 --pmc passes: a copy kernel of 64 MiB (read 64 MiB, write
     64 MiB) three times for the counters' scale, then mx4_moe_decode over 8 layers, twice."""
-    src = torch.ones(16 << 20, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        torch.add(src, 0.0, out=dst)
-    torch.cuda.synchronize()
+    copy_kernel_pass(torch)
     wl = synth.WORKLOADS["decode_t1"]
     layers = build_layers(moe, synth, torch, wl, "gemv", 8)
     for _ in range(2):
@@ -300,6 +299,35 @@ def counter_pass(moe, synth, torch):
             L.decode()
     torch.cuda.synchronize()
     log("counter pass done")
+
+
+def copy_kernel_pass(torch):
+    """A plain copy of known size (reads 64 MiB, writes 64 MiB) three times: the counters' scale."""
+    src = torch.ones(16 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+
+
+def counter_pass_prefill(moe, synth, torch):
+    """Workload of the rocprofv3 --pmc passes for the pp512 GEMMs: the copy kernel, then every
+    layer's chain twice with bf16 activations and twice with MXFP8 activations (4 layers, 1.7 GB
+    of experts, so no layer's weights are cache-resident from the previous one)."""
+    copy_kernel_pass(torch)
+    pw = synth.WORKLOADS["prefill_pp512"]
+    players = build_layers(moe, synth, torch, pw, "gemm", pw.layers)
+    for _ in range(2):
+        for L in players:
+            L.chain()
+    torch.cuda.synchronize()
+    for L in players:
+        L.alloc_mx8(torch)
+    for _ in range(2):
+        for L in players:
+            L.chain_mx8()
+    torch.cuda.synchronize()
+    log("prefill counter pass done")
 
 
 def main():
@@ -316,6 +344,9 @@ def main():
     torch.cuda.init()
     if args.counter_pass:
         counter_pass(moe, synth, torch)
+        return
+    if args.counter_pass_prefill:
+        counter_pass_prefill(moe, synth, torch)
         return
     sleep_cycles = sleep_cycles_for(torch, 20.0)
 
