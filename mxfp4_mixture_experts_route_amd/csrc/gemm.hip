@@ -137,8 +137,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmCtx& g, const f32x4_t (&
     // Values are the bf16-rounded SwiGLU-OAI outputs, scaled and encoded as mx8_quantize does.
     static_assert(WT == 2, "16 columns per wavefront, a block per wavefront pair");
     const int jb = g.tile_base[0];
-    const bool cols_live = jb < g.F;   // F % 32 == 0: both halves of the block exist or neither
-    const int blk = jb >> 5, nblk = g.F >> 5;
+    const int nblk = g.F >> 5;
     const int wave = g.tid >> 6;
     uint32_t* const amax_w = reinterpret_cast<uint32_t*>(g.xs + gemm_amax_off());
     uint32_t hp[NTT][2];   // the lane's 4 bf16 values, two per word
@@ -159,27 +158,50 @@ __device__ __forceinline__ void gemm_epilogue(const GemmCtx& g, const f32x4_t (&
       amax[tt] = a;
       if (lg == 0) amax_w[wave * (kGmTT * 16) + tt * 16 + lr] = a;
     }
-    __syncthreads();
+    __syncthreads();   // block maxima published; every wavefront is past the K loop
+    // codes and scale bytes go through LDS (the activation buffers, free now) and out as whole
+    // rows: stored straight from the lanes, 4-byte code pieces and single scale bytes each
+    // cost a whole write granule (3x the bytes in HBM writes)
+    constexpr int kPitch = 144;   // 128 code bytes + 16: rows 16 bytes apart in the banks
+    uint8_t* const stage = g.xs;
+    uint8_t* const stage_s = stage + kGmTT * 16 * kPitch;   // 4 scale bytes per row
+    const int jb0 = jb - wave * 16;                          // the slice's first column
+    const int cols = min(128, g.F - jb0);                    // a multiple of 32
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
       const int m = tt * 16 + lr;
       const uint32_t a = max(amax[tt], amax_w[(wave ^ 1) * (kGmTT * 16) + m]);
       const uint32_t sbyte = mx8_scale_byte(a);
       const float inv = mx8_inv_scale(sbyte);
-      if (m >= g.live || !cols_live) continue;
-      const size_t r = (size_t)(g.row0 + g.p0 + m);
       uint32_t pk = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         pk |= e4m3_rne_sat(bf16_bits_to_f32((hp[tt][i / 2] >> (16 * (i % 2))) & 0xFFFFu) * inv)
               << (8 * i);
-      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(g.out) + r * g.F + jb + 4 * lg) = pk;
-      if (lg == 0 && (wave & 1) == 0) {
-        uint8_t* srow = g.out_scale + r * g.spo;
-        srow[blk] = (uint8_t)sbyte;
-        if (blk == nblk - 1)
-          for (int p = nblk; p < g.spo; ++p) srow[p] = 0;   // the row's padding
+      *reinterpret_cast<uint32_t*>(stage + m * kPitch + wave * 16 + 4 * lg) = pk;
+      if (lg == 0 && (wave & 1) == 0) stage_s[m * 4 + (wave >> 1)] = (uint8_t)sbyte;
+    }
+    __syncthreads();
+    const int tid = g.tid;
+    for (int idx = tid; idx < NTT * 16 * 8; idx += 8 * 64) {   // 8 lanes x 16 bytes per row
+      const int m = idx >> 3, q = idx & 7;
+      if (m < g.live && q * 16 < cols) {
+        const size_t r = (size_t)(g.row0 + g.p0 + m);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(g.out) + r * g.F + jb0 + q * 16) =
+            *reinterpret_cast<const uint4*>(stage + m * kPitch + q * 16);
       }
+    }
+    for (int m = tid; m < NTT * 16; m += 8 * 64) {   // the row's scale bytes of this slice
+      if (m >= g.live) continue;
+      uint8_t* srow = g.out_scale + (size_t)(g.row0 + g.p0 + m) * g.spo;
+      const int b0 = jb0 >> 5, nb = cols >> 5;
+      if (nb == 4) {
+        *reinterpret_cast<uint32_t*>(srow + b0) = *reinterpret_cast<const uint32_t*>(stage_s + m * 4);
+      } else {
+        for (int b = 0; b < nb; ++b) srow[b0 + b] = stage_s[m * 4 + b];
+      }
+      if (b0 + nb == nblk)
+        for (int p = nblk; p < g.spo; ++p) srow[p] = 0;   // the row's padding
     }
     return;
   }
