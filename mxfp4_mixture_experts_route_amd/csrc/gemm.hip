@@ -425,7 +425,7 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
 constexpr int kMxThreads = 64 * kMxWaves;
 constexpr int kMxSC = 4;   // chunks per activation super-chunk
 __host__ __device__ constexpr int mx_wt(int act) { return act != MOE_ACT_NONE ? 2 : 3; }
-__host__ __device__ constexpr int mx_wring(int act) { return act != MOE_ACT_NONE ? 8 : 4; }
+__host__ __device__ constexpr int mx_wring(int act) { return act == MOE_ACT_SWIGLU_OAI_MX8 ? 4 : act != MOE_ACT_NONE ? 8 : 4; }
 constexpr int SRING_MAX = 2;   // scale groups in flight, at most (mx_wring / kMxSC)
 static_assert(gemm_dummy_off(true) == 2 * kMxSC * gemm_buf_bytes(kGmTT, true), "MX LDS layout");
 
