@@ -411,8 +411,9 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
 // MXFP8 pass on the MX-scaled MFMA. The arithmetic per byte is small here (no decode, one MFMA
 // per 16x16x128 tile product), so the pass is bound by keeping weight bytes in flight while the
 // matrix core works: 8 wavefronts, 2 per SIMD (one waits on memory while the other issues
-// MFMAs), each with a ring of weight chunks (SwiGLU: 8 chunks of 2 tiles, 16 KB; plain: 4 chunks
-// of 3 tiles, 12 KB). The activations move in super-chunks of 4 chunks, double-buffered in LDS,
+// MFMAs), each with a ring of weight chunks (SwiGLU: 8 chunks of 2 tiles, 16 KB, or 4 chunks
+// with the MXFP8 epilogue, whose extra live state would otherwise spill to scratch memory;
+// plain: 4 chunks of 3 tiles, 12 KB). The activations move in super-chunks of 4 chunks, double-buffered in LDS,
 // so the workgroup meets at a barrier once per 4 chunks; between barriers each wavefront
 // streams its own weights. B operands are read from LDS one token tile ahead of their MFMAs
 // (all of a chunk's at once would hold 8 x 8 registers).
