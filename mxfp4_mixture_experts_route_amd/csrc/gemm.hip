@@ -753,10 +753,11 @@ int gemm_launch(const void* a, const uint8_t* a_scale, const int32_t* a_row, int
                                             : (w->N + rows_per_wg - 1) / rows_per_wg;
   int64_t slots = mpad_max / tile_m;
   if (slots > w->E) slots = w->E;
-  // > 64 KB of dynamic LDS must be opted into, once per kernel, at the largest size used
-  static bool lds_attr_set = false;
+  // > 64 KB of dynamic LDS must be opted into, once per kernel and device, at the largest size
+  static bool lds_attr_set[kMaxDevices] = {};
   const int lds_max = gemm_lds_bytes(MX8);
-  if (!lds_attr_set) {
+  const int dslot = device_slot();
+  if (dslot < 0 || !lds_attr_set[dslot]) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MOE_ACT_NONE, MX8>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_max) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MOE_ACT_SWIGLU_OAI, MX8>),
@@ -766,7 +767,7 @@ int gemm_launch(const void* a, const uint8_t* a_scale, const int32_t* a_row, int
         hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MOE_ACT_SWIGLU_OAI_MX8, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_max) != hipSuccess)
       return MOE_ELAUNCH;
-    lds_attr_set = true;
+    if (dslot >= 0) lds_attr_set[dslot] = true;
   }
   const int lds = gemm_lds_bytes(MX8);
   // a 1-D grid of tiles (weight-row slice bx, expert slot), ordered per XCD in the kernel

@@ -7,6 +7,14 @@
 
 namespace moe {
 
+// Set-up a device keeps (a kernel's dynamic-LDS opt-in) is done once per device: call sites keep
+// a flag per device slot. Slot of the current device, or -1 (then the set-up simply repeats).
+constexpr int kMaxDevices = 64;
+inline int device_slot() {
+  int dev = 0;
+  return (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) ? dev : -1;
+}
+
 // Next pair of timing events, or false when timing is not armed (timing.hip).
 bool timing_next(hipEvent_t* start, hipEvent_t* stop);
 

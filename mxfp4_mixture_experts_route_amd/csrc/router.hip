@@ -224,13 +224,14 @@ extern "C" int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b
   if (mpad_max < need || mpad_max > 0x7FFFFFFFLL) return MOE_ESHAPE;
   if ((((uintptr_t)x) & 15) || (((uintptr_t)w_r) & 15)) return MOE_EALIGN;
   const size_t lds = moe::rt_lds_bytes(E, T * k);
-  static bool lds_attr_set = false;
-  if (!lds_attr_set) {
+  static bool lds_attr_set[moe::kMaxDevices] = {};   // > 64 KB of LDS: opt in once per device
+  const int dslot = moe::device_slot();
+  if (dslot < 0 || !lds_attr_set[dslot]) {
     const size_t most = moe::rt_lds_bytes(MOE_MAX_E, MOE_ROUTER_MAX_ROUTED);
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::router_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)most) != hipSuccess)
       return MOE_ELAUNCH;
-    lds_attr_set = true;
+    if (dslot >= 0) lds_attr_set[dslot] = true;
   }
   const int64_t blocks = (T + moe::kRtTok - 1) / moe::kRtTok;
   moe::launch(moe::router_kernel, dim3((unsigned)blocks), dim3(moe::kRtThreads), (unsigned)lds,
