@@ -122,6 +122,35 @@ struct GemmCtx {
   uint32_t sg[kGmMaxWT];   // the lane's row in a scale group (16 bytes: 4 chunks)
 };
 
+// Activation row that DMA slot m of the pass reads (a_row, or CSR order when a_row is NULL).
+// Slots without a routed row (m >= live) read the pass's first row and are pointed past the
+// resource by the caller: every lane loads, with no branch, so a wavefront issues all of its
+// row-id loads at once and the pass start waits for them together.
+__device__ __forceinline__ uint32_t gemm_src_row(const GemmCtx& g, int m, bool ok) {
+  const int r = g.row0 + g.p0 + (ok ? m : 0);
+  return g.a_row ? (uint32_t)g.a_row[r] : (uint32_t)r;
+}
+
+// Bias seeds of the lane's rows 4*lg..4*lg+3 of each weight tile (0 past the tile's rows or
+// without a bias); the loads are unconditional (clamped to row N - 1), so they issue together.
+template <int WT>
+__device__ __forceinline__ void gemm_bias(const GemmCtx& g, float (&b)[WT][4]) {
+#pragma unroll
+  for (int t = 0; t < WT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[t][i] = 0.0f;
+  if (!g.bias) return;
+  const float* be = g.bias + (size_t)g.e * g.N;
+#pragma unroll
+  for (int t = 0; t < WT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g.lg + i;
+      const float v = be[min(g.tile_base[t] + r, g.N - 1)];
+      b[t][i] = r < g.rows_in[t] ? v : 0.0f;
+    }
+}
+
 // Epilogue of a pass: lane holds rows 4*lg..4*lg+3 of each weight tile for token column lr.
 // SwiGLU: tiles [0, WT/2) are gate rows, tile t + WT/2 the matching up rows.
 template <int ACT, int NTT, int WT>
@@ -290,12 +319,9 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
     const int p = (wave + kGmWaves * i) * 64 + lane;
     const int m = p / PIECES;
     const int q = (p % PIECES) ^ (m & 15);
-    uint32_t off = kOOB;
-    if (m < g.live && wave + kGmWaves * i < KBS) {
-      const int r = g.row0 + g.p0 + m;
-      const uint32_t src = g.a_row ? (uint32_t)g.a_row[r] : (uint32_t)r;
-      off = src * (uint32_t)g.K * 2 + q * 16;
-    }
+    const bool ok = m < g.live && wave + kGmWaves * i < KBS;
+    const uint32_t src = gemm_src_row(g, m, ok);
+    const uint32_t off = ok ? src * (uint32_t)g.K * 2 + q * 16 : kOOB;
     xo[i] = off;
     // the last chunk may be narrower than 128 k
     xol[i] = (q * 8 < g.klast) ? off : kOOB;
@@ -316,16 +342,13 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
   };
 
   f32x4_t acc[kGmWT][NTT];
+  {
+    float b[kGmWT][4];
+    gemm_bias<kGmWT>(g, b);
 #pragma unroll
-  for (int t = 0; t < kGmWT; ++t) {
-    float b[4];
+    for (int t = 0; t < kGmWT; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * lg + i;
-      b[i] = (g.bias && r < g.rows_in[t]) ? g.bias[(size_t)g.e * g.N + g.tile_base[t] + r] : 0.0f;
-    }
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) acc[t][tt] = f32x4_t{b[0], b[1], b[2], b[3]};
+      for (int tt = 0; tt < NTT; ++tt) acc[t][tt] = f32x4_t{b[t][0], b[t][1], b[t][2], b[t][3]};
   }
 
   constexpr int kGmWRing = gemm_wring(kGmWT);
@@ -475,12 +498,9 @@ __device__ __forceinline__ void gemm_pass_mx8(const GemmCtx& g, uint8_t* __restr
     const int p = (wave + kMxWaves * i) * 64 + lane;
     const int m = p / PIECES;
     const int q = (p % PIECES) ^ gemm_swz8(m);
-    uint32_t off = kOOB;
-    if (m < g.live && wave + kMxWaves * i < KBS) {
-      const int r = g.row0 + g.p0 + m;
-      const uint32_t src = g.a_row ? (uint32_t)g.a_row[r] : (uint32_t)r;
-      off = src * (uint32_t)g.K + q * 16;
-    }
+    const bool ok = m < g.live && wave + kMxWaves * i < KBS;
+    const uint32_t src = gemm_src_row(g, m, ok);
+    const uint32_t off = ok ? src * (uint32_t)g.K + q * 16 : kOOB;
     xo[i] = off;
     xol[i] = (q * 16 < g.klast) ? off : kOOB;
   }
@@ -525,17 +545,23 @@ __device__ __forceinline__ void gemm_pass_mx8(const GemmCtx& g, uint8_t* __restr
   // that 16 consecutive rows read together into one or two banks)
   uint8_t* const xsc = xs + dummy + 1024;
   static_assert(kGmScalePitch == 128, "8 pieces per staged scale row");
-  for (int j = wave; j < NTT * 2; j += kMxWaves) {   // 1 KB = 8 rows per instruction
-    const int m = j * 8 + lane / 8;
+  // 1 KB = 8 rows per instruction, at most 2 per wavefront; row ids loaded together first
+  constexpr int NSC = (NTT * 2 + kMxWaves - 1) / kMxWaves;
+  uint32_t soff[NSC];
+#pragma unroll
+  for (int i = 0; i < NSC; ++i) {
+    const int m = (wave + kMxWaves * i) * 8 + lane / 8;
     const int piece = (lane % 8) ^ gemm_swz8(m);
-    uint32_t off = kOOB;
-    if (m < g.live && piece * 16 < g.spa) {
-      const int r = g.row0 + g.p0 + m;
-      const uint32_t src = g.a_row ? (uint32_t)g.a_row[r] : (uint32_t)r;
-      off = src * (uint32_t)g.spa + piece * 16;
-    }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        g.ras, (__attribute__((address_space(3))) void*)(xsc + j * 1024), 16, off, 0, 0, 0);
+    const bool ok = m < g.live && piece * 16 < g.spa;
+    const uint32_t src = gemm_src_row(g, m, ok);
+    soff[i] = ok ? src * (uint32_t)g.spa + piece * 16 : kOOB;
+  }
+#pragma unroll
+  for (int i = 0; i < NSC; ++i) {
+    const int j = wave + kMxWaves * i;   // uniform
+    if (j < NTT * 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          g.ras, (__attribute__((address_space(3))) void*)(xsc + j * 1024), 16, soff[i], 0, 0, 0);
   }
   issue_fence();
   load_x_super(0);
@@ -618,6 +644,9 @@ __device__ __forceinline__ void gemm_pass_mx8(const GemmCtx& g, uint8_t* __restr
 }
 
 __host__ __device__ constexpr int gemm_threads(bool mx8) { return mx8 ? kMxThreads : kGmThreads; }
+// Tile order by expert cost across the XCDs (bf16 activations, E <= 64); the MXFP8 variant
+// measured slower with it and keeps the id order
+__host__ __device__ constexpr bool gemm_balanced(int E, bool mx8) { return !mx8 && E <= kWave; }
 
 // Both variants: 8 wavefronts, 2 per SIMD (256 registers each)
 template <int ACT, bool MX8>
@@ -630,16 +659,47 @@ gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int
             uint8_t* __restrict__ out_scale, int nbx, int nslots, int per_xcd) {
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   // XCD-aware tile order: the hardware deals workgroup ids to the 8 XCDs round robin, so id L
-  // runs on XCD L % 8; virtual tile v = (L % 8) * per_xcd + L / 8 gives every XCD a contiguous
-  // run of tiles, i.e. whole experts (bx fastest), and its L2 then holds the activation rows of
-  // the one or two experts it is working on instead of every expert's
+  // runs on XCD L % 8, and the L / 8-th workgroup of an XCD takes its tile (bx fastest), so each
+  // XCD works through whole experts and its L2 holds the activation rows of the one or two
+  // experts it is on instead of every expert's.
+  //  * E <= 64: experts go to XCDs by cost, so that no XCD is left with the heavy ones while the
+  //    others idle. Every workgroup ranks the live experts by cost (token tiles plus two per
+  //    pass, for its set-up and drain; ties by id) from the counts, the same ranking everywhere,
+  //    and rank r is position r / 8 on XCD r % 8, or 7 - r % 8 in odd rounds (a snake); heavy
+  //    experts come first on each XCD, light ones fill the tail.
+  //  * E > 64: live experts in id order, each XCD a contiguous run of tiles.
   const int L = (int)blockIdx.x;
-  const int v = (L % kXcds) * per_xcd + L / kXcds;
-  if (v >= nbx * nslots) return;
-  const int bxi = v % nbx, slot = v / nbx;
-  const int c64 = ((int)(threadIdx.x & 63) < E) ? counts[threadIdx.x & 63] : 0;
-  const int e = wave_slot_expert(counts, E, slot, c64);
-  if (e < 0) return;   // uniform over the workgroup: fewer live experts than slots
+  const int xcd = L % kXcds, idx = L / kXcds;
+  const int lane0 = (int)(threadIdx.x & 63);
+  // each lane: count and padded base of expert lane, loaded together
+  const int c64 = lane0 < E ? counts[lane0] : 0;
+  const int b64 = lane0 < E ? basep[lane0] : 0;
+  int e, bxi, row0, cnt;
+  if (gemm_balanced(E, MX8)) {
+    const int pos = idx / nbx;
+    bxi = idx - pos * nbx;
+    const int passes = (c64 + kGmTT * 16 - 1) / (kGmTT * 16);
+    const int cost = c64 > 0 ? (c64 + 15) / 16 + 2 * passes : 0;
+    int rank = 0;
+    for (int j = 0; j < E; ++j) {
+      const int cj = __builtin_amdgcn_readlane(cost, j);
+      rank += (cj > cost) | ((cj == cost) & (j < lane0));
+    }
+    const int r = kXcds * pos + ((pos & 1) ? kXcds - 1 - xcd : xcd);
+    const uint64_t hit = __ballot(cost > 0 && rank == r);
+    if (hit == 0) return;   // uniform over the workgroup: fewer live experts than positions
+    e = __ffsll((unsigned long long)hit) - 1;
+    row0 = __builtin_amdgcn_readlane(b64, e);
+    cnt = __builtin_amdgcn_readlane(c64, e);
+  } else {
+    const int v = xcd * per_xcd + idx;
+    if (v >= nbx * nslots) return;
+    bxi = v % nbx;
+    e = wave_slot_expert(counts, E, v / nbx, c64);
+    if (e < 0) return;   // uniform over the workgroup: fewer live experts than slots
+    row0 = basep[e];
+    cnt = counts[e];
+  }
   constexpr bool swiglu = (ACT != MOE_ACT_NONE);
   GemmCtx g;
   g.a_row = a_row;
@@ -664,8 +724,7 @@ gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int
   const int lane = g.tid & 63, wave = g.tid >> 6;
   g.lr = lane & 15;
   g.lg = lane >> 4;
-  g.row0 = basep[e];
-  const int cnt = counts[e];
+  g.row0 = row0;
 
   // weight rows of the wavefront's tiles (first row, rows that exist). A workgroup covers 128
   // h columns (SwiGLU: each wavefront's gate tiles [0, WT/2) and the matching up tiles) or 384
@@ -770,9 +829,11 @@ int gemm_launch(const void* a, const uint8_t* a_scale, const int32_t* a_row, int
     if (dslot >= 0) lds_attr_set[dslot] = true;
   }
   const int lds = gemm_lds_bytes(MX8);
-  // a 1-D grid of tiles (weight-row slice bx, expert slot), ordered per XCD in the kernel
-  const int64_t tiles = bx * slots;
-  const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
+  // a 1-D grid of tiles (weight-row slice bx, expert slot), ordered per XCD in the kernel:
+  // whole experts per XCD (E <= 64: positions of ceil(slots / 8) experts), else a contiguous
+  // share of the tiles
+  const int64_t per_xcd = gemm_balanced(w->E, MX8) ? (slots + kXcds - 1) / kXcds * bx
+                                                   : (bx * slots + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds)), block(gemm_threads(MX8));
   if (act == MOE_ACT_SWIGLU_OAI)
     launch(gemm_kernel<MOE_ACT_SWIGLU_OAI, MX8>, grid, block, lds, stream, a, a_scale,
