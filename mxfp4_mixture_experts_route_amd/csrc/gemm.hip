@@ -352,6 +352,10 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
   }
 
   constexpr int kGmWRing = gemm_wring(kGmWT);
+  // B fragments in flight (LDS reads ahead of their MFMAs), on the SwiGLU passes of up to
+  // kBRingTT token tiles; the plain passes (3 weight tiles) have no registers to spare for it
+  constexpr int kBD = 4;
+  constexpr int kBRingTT = swiglu ? 6 : 0;
   u32x4_t wq[kGmWRing][kGmWT];
   uint32_t wx[kGmWRing][kGmWT];
 
@@ -404,19 +408,53 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
         float cs[kGmWT];
 #pragma unroll
         for (int t = 0; t < kGmWT; ++t) cs[t] = e8m0_scale_operand(wx[sl][t]);
+        auto read_b = [&](int i, int tt) {
+          const int m = tt * 16 + lr;   // m % 16 == lr
+          return *reinterpret_cast<const bf16x8_t*>(xb + (m * 16 + ((lg * 4 + i) ^ swz)) * 16);
+        };
+        if constexpr (NTT <= kBRingTT) {
+          // the chunk's steps st = (k substep i, token tile tt), i major; the B fragment of
+          // step st is read from LDS kBD steps ahead into a ring, so each read has kBD - 1
+          // steps of MFMAs to land (read at use, it was waited for with two MFMAs in flight)
+          constexpr int NS = 4 * NTT;
+          bf16x8_t Bq[kBD];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16x8_t A[kGmWT];
+          for (int st = 0; st < kBD && st < NS; ++st) Bq[st] = read_b(st / NTT, st % NTT);
+          // A of substep i + 1 is decoded after the first step's MFMAs of substep i (a second
+          // set of A registers), so the converts overlap the matrix core instead of holding up
+          // the substep's first MFMA
+          bf16x8_t A[2][kGmWT];
 #pragma unroll
-          for (int t = 0; t < kGmWT; ++t) A[t] = dequant8(wq[sl][t][i], cs[t]);
+          for (int t = 0; t < kGmWT; ++t) A[0][t] = dequant8(wq[sl][t][0], cs[t]);
 #pragma unroll
-          for (int tt = 0; tt < NTT; ++tt) {
-            const int m = tt * 16 + lr;   // m % 16 == lr
-            const bf16x8_t B =
-                *reinterpret_cast<const bf16x8_t*>(xb + (m * 16 + ((lg * 4 + i) ^ swz)) * 16);
+          for (int st = 0; st < NS; ++st) {
+            const int i = st / NTT, tt = st % NTT;
 #pragma unroll
             for (int t = 0; t < kGmWT; ++t)
-              acc[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t], B, acc[t][tt], 0, 0, 0);
+              acc[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i & 1][t], Bq[st % kBD],
+                                                                  acc[t][tt], 0, 0, 0);
+            if (st + kBD < NS) Bq[st % kBD] = read_b((st + kBD) / NTT, (st + kBD) % NTT);
+            if (tt == 0 && i < 3) {
+#pragma unroll
+              for (int t = 0; t < kGmWT; ++t)
+                A[(i + 1) & 1][t] = dequant8(wq[sl][t][i + 1], cs[t]);
+            }
+            // keeps each read at its step (the scheduler would sink them to their use)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bf16x8_t A[kGmWT];
+#pragma unroll
+            for (int t = 0; t < kGmWT; ++t) A[t] = dequant8(wq[sl][t][i], cs[t]);
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+              const bf16x8_t B = read_b(i, tt);
+#pragma unroll
+              for (int t = 0; t < kGmWT; ++t)
+                acc[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t], B, acc[t][tt], 0, 0, 0);
+            }
           }
         }
       }
