@@ -86,10 +86,17 @@ struct Mx4Wave {
   u32x4_t wq[SEG];
   uint32_t sc[SEG];
 
-  // Rows of expert e: this lane streams row n (if valid) of an [E][N][K] chunked stack, over
-  // chunks [.., ce_) of the C chunks of K.
+  // Rows of expert e (the same on every lane of the wavefront): this lane streams row n (if
+  // valid) of an [E][N][K] chunked stack, over chunks [.., ce_) of the C chunks of K.
   __device__ __forceinline__ void init(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
                                        int e, int n, bool valid, int N_, int K, int ce_) {
+    // e (and the K range, from the wavefront index) arrive in vector registers; read as scalars,
+    // the buffer resources and scalar offsets below are scalars too (one in vector registers
+    // makes the compiler wrap every load of the segment in a loop over the lanes' values)
+    e = __builtin_amdgcn_readfirstlane(e);
+    N_ = __builtin_amdgcn_readfirstlane(N_);
+    K = __builtin_amdgcn_readfirstlane(K);
+    ce_ = __builtin_amdgcn_readfirstlane(ce_);
     const int lane = (int)(threadIdx.x & 63);
     lg = lane >> 4;
     N = N_;
@@ -110,6 +117,7 @@ struct Mx4Wave {
   // another expert's scales, where a NaN byte would poison 0 * scale). The
   // scheduling barriers keep the issue order (the compiler would move the scale loads last).
   __device__ __forceinline__ void load_segment(int c0) {
+    c0 = __builtin_amdgcn_readfirstlane(c0);   // uniform: the chunk offsets ride in soffset
 #pragma unroll
     for (int i = 0; i < SEG / 4; ++i) {
       const int gi = (c0 + 4 * i) / 4;   // c0 is a multiple of 4: whole groups
