@@ -105,19 +105,26 @@ __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
   const int t = rho / k, slot = rho - t * k;
   const uint32_t row_bytes = (uint32_t)K * 2;
 
-  // 1. token t's logits, then its activation row copied to LDS (LDS-DMA), then routing: the
-  // wavefront's expert is pick `slot` of the token's top-k
+  // 1. token t's activation row copied to LDS (LDS-DMA), then routing: the wavefront's expert
+  // is pick `slot` of the token's top-k. For E <= 64 the logits row comes by LDS-DMA too, into
+  // this wavefront's own 256 bytes of the (not yet used) K-part area, so one wait lands both
+  // copies (a vector load of the logits was waited for before the copy went out: two round
+  // trips before the first weight load instead of one)
+  lds_dma_copy(x + (size_t)t * K, row_bytes, xs, wave, nthreads >> 6);
+  __builtin_amdgcn_sched_barrier(0);
   int e;
   if (E <= kWave) {   // one logit per lane: rank by broadcast compares
-    const float v = lane < E ? logits[(size_t)t * E + lane] : 0.0f;
-    lds_dma_copy(x + (size_t)t * K, row_bytes, xs, wave, nthreads >> 6);
-    __builtin_amdgcn_sched_barrier(0);
+    const size_t zoff = ((size_t)row_bytes + 1023) & ~(size_t)1023;
+    float* lrow = reinterpret_cast<float*>(xs + zoff + 64 + (size_t)wave * 1024);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(logits + (size_t)t * E, (uint32_t)E * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rl, (__attribute__((address_space(3))) void*)lrow, 4, (uint32_t)lane * 4, 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    const float v = lrow[lane];   // 0 past E (read past the resource)
     e = rank_pick(wave_rank_small(v, E), slot);
   } else {
     float lv[kRoutePerLane];
     wave_topk_load(logits + (size_t)t * E, E, lv);
-    lds_dma_copy(x + (size_t)t * K, row_bytes, xs, wave, nthreads >> 6);
-    __builtin_amdgcn_sched_barrier(0);
     int my_id;
     float my_v;
     wave_topk_select(lv, E, k, my_id, my_v);
@@ -528,8 +535,9 @@ extern "C" int mx4_moe_decode(const float* logits, const uint16_t* x, int64_t T,
   int upw1 = 256 / 64 / ks1;
   while (upw1 > 1 && waves_total / (upw1 * ks1) < 640) upw1 >>= 1;
   const int waves1 = upw1 * ks1;
-  const size_t lds1 = (((size_t)D * 2 + 1023) & ~(size_t)1023) + 64 +
-                      (ks1 > 1 ? (size_t)waves1 * 64 * 16 : 0);
+  // x row, zero block, then 1 KB per wavefront: K-part sums, and first each wavefront's copy of
+  // the logits row (E <= 64)
+  const size_t lds1 = (((size_t)D * 2 + 1023) & ~(size_t)1023) + 64 + (size_t)waves1 * 64 * 16;
   // launch 2: one workgroup per (16 rows, token), ksplit wavefronts per slot
   int ks2 = moe::gv_ksplit(C2);
   while (ks2 > 1 && k * ks2 * 64 > moe::kDecMaxThreads) --ks2;
