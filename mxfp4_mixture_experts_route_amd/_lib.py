@@ -44,6 +44,12 @@ def lib() -> ctypes.CDLL:
     """Load the HIP library once; raises if it has not been built."""
     global _lib
     if _lib is None:
+        # torch first: the library and torch must share one HIP runtime. Both runtimes carry the
+        # soname libamdhip64.so.7, and the process keeps whichever is loaded first; loaded
+        # first, the library (RUNPATH: the system ROCm) would put torch on a runtime other than
+        # the one it ships with, and launches then fail (launches rejected, then a crash in
+        # torch's own copies)
+        _torch()
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m mxfp4_mixture_experts_route_amd.build`")

@@ -18,9 +18,13 @@ inline int device_slot() {
 // Next pair of timing events, or false when timing is not armed (timing.hip).
 bool timing_next(hipEvent_t* start, hipEvent_t* stop);
 
+// The runtime's last-error state is cleared first: entry points report MOE_ELAUNCH from
+// hipGetLastError() after the launch, and an error left by an earlier, unrelated runtime call
+// (the caller's, or a framework's start-up) must not be reported as this launch's.
 template <typename Kernel, typename... Args>
 inline void launch(Kernel kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
                    Args... args) {
+  (void)hipGetLastError();
   hipEvent_t start, stop;
   if (timing_next(&start, &stop))
     hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, start, stop, 0u, args...);

@@ -255,3 +255,25 @@ def test_decode_persistent_argument_checks():
     assert call(T=17) == _lib.MOE_ESHAPE
     assert call(dn=experts(E=8, N=32, K=64)) == _lib.MOE_ESHAPE
     assert call(ws=ctypes.c_void_p(0x1002)) == _lib.MOE_EALIGN
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    """In a fresh process whose first use of the package loads the library (torch not yet
+    imported), exactly one HIP runtime is mapped, and it is the one torch ships with: the
+    library's own first load would otherwise map the system runtime and torch would then run on
+    it (one soname, so the first one loaded wins)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from mxfp4_mixture_experts_route_amd import _lib\n"
+            "assert 'torch' not in sys.modules\n"
+            "_lib.lib()\n"
+            "import os, torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "tdir = os.path.realpath(os.path.join(os.path.dirname(torch.__file__), 'lib'))\n"
+            "print(sorted(maps)); print(tdir)\n"
+            "assert len(maps) == 1, maps\n"
+            "assert os.path.realpath(maps.pop()).startswith(tdir + os.sep)\n") % root
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr

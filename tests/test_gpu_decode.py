@@ -41,6 +41,9 @@ CASES = {
     "single_expert": dict(seed=25, E=1, D=32, F=32, T=2, k=1),
     "ksplit_both": dict(seed=26, E=6, D=1600, F=416, T=2, k=3),     # D: 13 chunks (split)
     "long_ffn": dict(seed=27, E=4, D=96, F=1664, T=1, k=2),         # F: 13 chunks (split)
+    # routing inside the gate_up launch: logits row by LDS-DMA for E <= 64, loaded per lane above
+    "E64_k4": dict(seed=29, E=64, D=64, F=64, T=3, k=4),
+    "E128_k4": dict(seed=30, E=128, D=64, F=64, T=2, k=4),
 }
 
 

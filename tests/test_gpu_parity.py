@@ -130,6 +130,19 @@ def test_bucket_edge_shapes_bit_exact(T, k, E, tile_m, skew):
         assert np.array_equal(g, r), nm
 
 
+def test_stale_runtime_error_is_not_a_launch_failure():
+    """An error state left in the HIP runtime by an earlier, unrelated call (a host-side
+    hipSetDevice with an invalid ordinal) is not reported as the next call's launch failure."""
+    import ctypes
+    hip_path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line)
+    hip = ctypes.CDLL(hip_path)
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+    ids = synth.random_ids(5, 4, 2, 8)
+    mpad, _, got = front(ids, 8, 16)   # raised MoeError(MOE_ELAUNCH) on the stale error
+    for nm, g, r in zip(("counts", "basep", "row_tok", "pos"), got, oracle.bucket(ids, 8, 16, mpad)):
+        assert np.array_equal(g, r), nm
+
+
 def test_route_ties_and_signed_zero():
     logits = np.array([[1.0, 3.0, 3.0, -1.0], [-1.0, 0.0, -0.0, -2.0], [0.25] * 4,
                        [-0.0, 0.0, -0.0, 0.0]], dtype=np.float32)
@@ -299,6 +312,12 @@ EDGE = {
     "m136_and_32": dict(seed=10, E=4, D=64, F=96, T=168, k=1, tile_m=16,
                         ids=skewed_ids([0, 136, 0, 32], 10)),
     "tile_m_32": dict(seed=7, E=16, D=64, F=96, T=70, k=4, tile_m=32),
+    # the GEMM deals experts to XCDs by cost for E <= 64 and in id order above: both sides of
+    # the boundary, with every expert live and with fewer live experts than placement slots
+    "E64_cost_order": dict(seed=12, E=64, D=64, F=64, T=200, k=4, tile_m=16),
+    "E65_id_order": dict(seed=13, E=65, D=64, F=64, T=200, k=4, tile_m=16),
+    "E64_few_live": dict(seed=14, E=64, D=64, F=96, T=40, k=1, tile_m=16,
+                         ids=skewed_ids([0] * 50 + [7, 5, 0, 9, 3, 0, 11, 5] + [0] * 6, 14)),
 }
 
 
