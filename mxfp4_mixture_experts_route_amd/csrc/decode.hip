@@ -105,31 +105,37 @@ __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
   const int t = rho / k, slot = rho - t * k;
   const uint32_t row_bytes = (uint32_t)K * 2;
 
-  // 1. token t's activation row copied to LDS (LDS-DMA), then routing: the wavefront's expert
-  // is pick `slot` of the token's top-k. For E <= 64 the logits row comes by LDS-DMA too, into
-  // this wavefront's own 256 bytes of the (not yet used) K-part area, so one wait lands both
-  // copies (a vector load of the logits was waited for before the copy went out: two round
-  // trips before the first weight load instead of one)
+  // 1. token t's activation row copied to LDS (LDS-DMA), then routing: the workgroup's expert is
+  // pick `slot` of the token's top-k. Wavefront 0 alone routes and leaves the pick in LDS (in the
+  // spare bytes of its own K-part slot, which it never writes: it holds part 0): every wavefront
+  // would compute the same pick. For E <= 64 the logits row comes by LDS-DMA too, right after
+  // the copy, so one wait lands both, and the rank reads it from LDS.
   lds_dma_copy(x + (size_t)t * K, row_bytes, xs, wave, nthreads >> 6);
   __builtin_amdgcn_sched_barrier(0);
-  int e;
-  if (E <= kWave) {   // one logit per lane: rank by broadcast compares
-    const size_t zoff = ((size_t)row_bytes + 1023) & ~(size_t)1023;
-    float* lrow = reinterpret_cast<float*>(xs + zoff + 64 + (size_t)wave * 1024);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(logits + (size_t)t * E, (uint32_t)E * 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rl, (__attribute__((address_space(3))) void*)lrow, 4, (uint32_t)lane * 4, 0, 0, 0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    const float v = lrow[lane];   // 0 past E (read past the resource)
-    e = rank_pick(wave_rank_small(v, E), slot);
-  } else {
-    float lv[kRoutePerLane];
-    wave_topk_load(logits + (size_t)t * E, E, lv);
-    int my_id;
-    float my_v;
-    wave_topk_select(lv, E, k, my_id, my_v);
-    e = __shfl(my_id, slot);
+  const size_t zoff = ((size_t)row_bytes + 1023) & ~(size_t)1023;
+  uint8_t* const slot0 = xs + zoff + 64;   // wavefront 0's 1 KB: logits, then the pick at +512
+  int* const pick = reinterpret_cast<int*>(slot0 + 512);
+  if (wave == 0) {
+    int e0;
+    if (E <= kWave) {   // one logit per lane: rank by broadcast compares
+      float* lrow = reinterpret_cast<float*>(slot0);
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(logits + (size_t)t * E, (uint32_t)E * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rl, (__attribute__((address_space(3))) void*)lrow, 4, (uint32_t)lane * 4, 0, 0, 0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      e0 = rank_pick(wave_rank_lds(lrow, E), slot);   // lrow: 0 past E (read past the resource)
+    } else {
+      float lv[kRoutePerLane];
+      wave_topk_load(logits + (size_t)t * E, E, lv);
+      int my_id;
+      float my_v;
+      wave_topk_select(lv, E, k, my_id, my_v);
+      e0 = __shfl(my_id, slot);
+    }
+    if (lane == 0) *pick = e0;
   }
+  __syncthreads();   // the pick is published (and every wavefront's share of the copy landed)
+  const int e = *pick;
 
   // 2. 16 rows (gate rows j..j+7 and the matching up rows) and a part of K per wavefront
   const int part = wave % ksplit;

@@ -87,6 +87,25 @@ __device__ __forceinline__ int wave_rank_small(float v, int E) {
   return lane < E ? rank : E + lane;
 }
 
+// The same ranks from the logits row staged in LDS (row[0..63], E <= 64; what lies past E is
+// never compared): eight values per step come as broadcast LDS reads and every compare is
+// independent of the previous one, so the steps overlap. (wave_rank_small's steps each wait for
+// a cross-lane read into a scalar register: ~115 cycles a step, 1.5 us for E = 32.)
+__device__ __forceinline__ int wave_rank_lds(const float* row, int E) {
+  const int lane = (int)(threadIdx.x & 63);
+  const float v = row[lane];
+  int rank = 0;
+  for (int j0 = 0; j0 < E; j0 += 8) {
+    const float4 a = *reinterpret_cast<const float4*>(row + j0);
+    const float4 b = *reinterpret_cast<const float4*>(row + j0 + 4);
+    const float vj[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      rank += (j0 + u < E && ranks_before(vj[u], j0 + u, v, lane)) ? 1 : 0;
+  }
+  return lane < E ? rank : E + lane;
+}
+
 // Expert of pick `slot` from wave_rank_small ranks (uniform).
 __device__ __forceinline__ int rank_pick(int rank, int slot) {
   return __ffsll((unsigned long long)__ballot(rank == slot)) - 1;
