@@ -342,7 +342,7 @@ __device__ __forceinline__ void down_item_persistent(
   float wsl = 0.0f;   // wavefront 0, lane sl: routing weight of slot sl
   if (E <= kWave) {
     const float v = lane < E ? logits[(size_t)t * E + lane] : 0.0f;
-    const int rank = wave_rank_small(v, E);
+    const int rank = wave_rank_row(logits + (size_t)t * E, E);
     e = rank_pick(rank, slot);
     if (wave == 0) {
       int my_id = 0;

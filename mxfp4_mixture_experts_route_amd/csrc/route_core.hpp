@@ -73,24 +73,12 @@ __device__ __forceinline__ void wave_topk_select(const float (&v)[kRoutePerLane]
   }
 }
 
-// E <= 64: lane e holds logit e (v, loaded by the caller; anything for lanes >= E). Each lane
-// counts the logits that rank before its own (a broadcast of every lane's value through
-// v_readlane, no LDS and no dependent shuffle chains); the lane of rank r is pick r. Returns
-// this lane's rank (E or more for lanes >= E).
-__device__ __forceinline__ int wave_rank_small(float v, int E) {
-  const int lane = (int)(threadIdx.x & 63);
-  int rank = 0;
-  for (int j = 0; j < E; ++j) {
-    const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
-    rank += ranks_before(vj, j, v, lane) ? 1 : 0;
-  }
-  return lane < E ? rank : E + lane;
-}
-
-// The same ranks from the logits row staged in LDS (row[0..63], E <= 64; what lies past E is
-// never compared): eight values per step come as broadcast LDS reads and every compare is
-// independent of the previous one, so the steps overlap. (wave_rank_small's steps each wait for
-// a cross-lane read into a scalar register: ~115 cycles a step, 1.5 us for E = 32.)
+// E <= 64: the rank of every lane's logit among the row's E logits (the number that rank before
+// it), the lane of rank r holding pick r; E or more for lanes >= E. From the logits row staged in
+// LDS (row[0..63]; what lies past E is never compared): eight values per step come as broadcast
+// LDS reads and every compare is independent of the previous one, so the steps overlap. (A
+// broadcast of each lane's value by v_readlane waits for the scalar register every step:
+// ~115 cycles a step, 1.5 us for E = 32.)
 __device__ __forceinline__ int wave_rank_lds(const float* row, int E) {
   const int lane = (int)(threadIdx.x & 63);
   const float v = row[lane];
@@ -106,7 +94,26 @@ __device__ __forceinline__ int wave_rank_lds(const float* row, int E) {
   return lane < E ? rank : E + lane;
 }
 
-// Expert of pick `slot` from wave_rank_small ranks (uniform).
+// The same ranks from a logits row in memory (global or LDS; E <= 64): eight values per step
+// by loads every lane makes at the same address, then the tail one at a time, so nothing past
+// E is read and the compares are independent of each other (no cross-lane step in the chain).
+__device__ __forceinline__ int wave_rank_row(const float* __restrict__ row, int E) {
+  const int lane = (int)(threadIdx.x & 63);
+  const float v = lane < E ? row[lane] : 0.0f;
+  int rank = 0;
+  int j0 = 0;
+  for (; j0 + 8 <= E; j0 += 8) {
+    float vj[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) vj[u] = row[j0 + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rank += ranks_before(vj[u], j0 + u, v, lane) ? 1 : 0;
+  }
+  for (; j0 < E; ++j0) rank += ranks_before(row[j0], j0, v, lane) ? 1 : 0;
+  return lane < E ? rank : E + lane;
+}
+
+// Expert of pick `slot` from wave_rank_lds / wave_rank_row ranks (uniform).
 __device__ __forceinline__ int rank_pick(int rank, int slot) {
   return __ffsll((unsigned long long)__ballot(rank == slot)) - 1;
 }
@@ -116,7 +123,7 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
   if (E <= kWave) {
     const int lane = (int)(threadIdx.x & 63);
     const float v = lane < E ? row[lane] : 0.0f;
-    const int rank = wave_rank_small(v, E);
+    const int rank = wave_rank_row(row, E);
     my_id = 0;
     my_v = 0.0f;
     for (int r = 0; r < k; ++r) {
