@@ -243,10 +243,12 @@ decode_down_kernel(const uint16_t* __restrict__ h, int k, const int32_t* __restr
   const int t = (int)blockIdx.y, unit = (int)blockIdx.x;
   const uint32_t row_bytes = (uint32_t)F * 2;
 
-  // 1. the token's k rows of h (routed-row order: slot s is row t*k + s) to LDS, then this
-  // wavefront's slot and expert
-  const int slot = wave / ksplit, part = wave % ksplit;
-  const int e = ids[t * k + slot];
+  // 1. the token's k rows of h (routed-row order: slot s is row t*k + s) to LDS, and this
+  // wavefront's slot and expert. The expert id comes through the scalar cache, counted apart
+  // from the copy: the weights go out as soon as it arrives (a vector load of it was waited for
+  // together with the whole copy, whose trip count the compiler does not know)
+  const int slot = __builtin_amdgcn_readfirstlane(wave / ksplit), part = wave % ksplit;
+  const int e = ((const __attribute__((address_space(4))) int32_t*)ids)[t * k + slot];
   lds_dma_copy(h + (size_t)t * k * F, (uint32_t)k * row_bytes, xs, wave, nthreads >> 6);
   __builtin_amdgcn_sched_barrier(0);
   int cb, ce, Cp;
