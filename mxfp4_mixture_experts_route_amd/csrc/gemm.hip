@@ -718,10 +718,19 @@ gemm_kernel(const void* __restrict__ a, const uint8_t* __restrict__ a_scale, int
     bxi = idx - pos * nbx;
     const int passes = (c64 + kGmTT * 16 - 1) / (kGmTT * 16);
     const int cost = c64 > 0 ? (c64 + 15) / 16 + 2 * passes : 0;
+    // every expert's cost to this wavefront's own 256 bytes of the LDS (unused before the first
+    // pass), then eight compares per step against broadcast reads of it, independent of each
+    // other (a v_readlane broadcast per expert waits for its scalar register every step)
+    int* const cl = reinterpret_cast<int*>(xs) + (threadIdx.x >> 6) * kWave;
+    cl[lane0] = cost;
     int rank = 0;
-    for (int j = 0; j < E; ++j) {
-      const int cj = __builtin_amdgcn_readlane(cost, j);
-      rank += (cj > cost) | ((cj == cost) & (j < lane0));
+    for (int j0 = 0; j0 < E; j0 += 8) {
+      const int4 a = *reinterpret_cast<const int4*>(cl + j0);
+      const int4 b = *reinterpret_cast<const int4*>(cl + j0 + 4);
+      const int cj[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        rank += (int)((j0 + u < E) & ((cj[u] > cost) | ((cj[u] == cost) & (j0 + u < lane0))));
     }
     const int r = kXcds * pos + ((pos & 1) ? kXcds - 1 - xcd : xcd);
     const uint64_t hit = __ballot(cost > 0 && rank == r);
