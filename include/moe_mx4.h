@@ -66,6 +66,9 @@ typedef enum {
   MOE_EALIGN = 3,  /* weights, activations or outputs not 16-byte aligned                      */
   MOE_ELAUNCH = 4  /* the HIP runtime reported an error when the kernel was enqueued          */
 } moe_status;
+/* Launch errors are read with hipGetLastError() right after each launch, and the runtime's
+   last-error state is cleared just before it: an error left there by an earlier, unrelated call
+   of the caller's is consumed by the next entry point and not reported as its own. */
 
 typedef enum {
   MOE_ACT_NONE = 0,       /* out = f32 [mpad_max][N]: bias + a . W^T                              */
