@@ -8,9 +8,10 @@
 //
 // At decode sizes every launch costs microseconds of ramp and drain, which at T = 1 is as much
 // as the route, bucket and combine work itself. Here:
-//  * Launch 1: every workgroup of routed row rho = t*k + s routes token t itself (each
-//    wavefront: for E <= 64 the rank of every logit by broadcast compares, else k rounds of
-//    arg-best over the E logits), takes pick s as its expert and runs the
+//  * Launch 1: every workgroup of routed row rho = t*k + s routes token t itself (its
+//    wavefront 0: for E <= 64 the rank of every logit against the row staged in LDS, else k
+//    rounds of arg-best over the E logits; the pick goes to the others through LDS), takes
+//    pick s as its expert and runs the
 //    gate_up projection + clamped SwiGLU-OAI for that row with the wavefront engine of
 //    gemv_core.hpp; h is written in routed-row order. One extra workgroup writes the routing
 //    (ids, w) and the CSR of tile 1 (counts, basep, row_tok, pos) for the caller.
@@ -117,7 +118,7 @@ __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
   int* const pick = reinterpret_cast<int*>(slot0 + 512);
   if (wave == 0) {
     int e0;
-    if (E <= kWave) {   // one logit per lane: rank by broadcast compares
+    if (E <= kWave) {   // one logit per lane: rank against the row in LDS
       float* lrow = reinterpret_cast<float*>(slot0);
       const __amdgpu_buffer_rsrc_t rl = make_rsrc(logits + (size_t)t * E, (uint32_t)E * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
