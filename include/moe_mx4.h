@@ -43,7 +43,7 @@
  *   - `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues work on it and
  *     returns; nothing synchronizes. Buffers must stay alive until the stream reaches the work.
  *   - Arguments are validated on the host before anything is enqueued; on any error nothing is
- *     enqueued and the status says why. Data preconditions (finite logits, ids in [0,E), a CSR
+ *     enqueued and the status says why. Data preconditions (ids in [0,E), a CSR
  *     produced by moe_bucket with the same E/tile_m/mpad_max) are documented, not checked.
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
  *   - Results are deterministic: two identical calls produce bit-identical outputs (no float
@@ -99,11 +99,16 @@ int64_t moe_mpad_max(int64_t T, int k, int E, int tile_m);
 
 /*
  * Top-k routing ([chain]: expert ids per token; [mx4]: k = 4 experts per token at gpt-oss shape).
- *   logits  f32 [T][E], row-major, finite.
+ *   logits  f32 [T][E], row-major.
  *   ids     i32 [T][k] out: for each token, the k largest logits in descending order; equal logits
- *           are ordered by ascending expert id (-0.0 and +0.0 are equal).
+ *           are ordered by ascending expert id (-0.0 and +0.0 are equal). A NaN logit ranks below
+ *           every number (-inf included), NaNs among themselves by id: the order is total, so
+ *           every row, NaN rows included, yields k distinct ids in [0, E) (the pages route finite
+ *           logits; this reading only makes any input safe). Every call that routes (moe_router,
+ *           mx4_moe_decode, mx4_moe_decode_persistent) uses this same order.
  *   w       f32 [T][k] out: softmax over the k selected logits,
- *           w[s] = exp(l[s]-l[0]) / sum_j exp(l[j]-l[0]), evaluated in double and rounded to f32.
+ *           w[s] = exp(l[s]-l[0]) / sum_j exp(l[j]-l[0]), evaluated in double and rounded to f32
+ *           (NaN where a NaN logit is among the k).
  * Errors: MOE_EINVAL for NULL pointers, T < 1, E < 1, k < 1, k > min(E, MOE_MAX_K);
  *         MOE_ESHAPE for E > MOE_MAX_E.
  */

@@ -136,7 +136,10 @@ __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
     if (lane == 0) *pick = e0;
   }
   __syncthreads();   // the pick is published (and every wavefront's share of the copy landed)
-  const int e = *pick;
+  // the top-k order is total (route_core.hpp), so the pick is an expert of [0, E) whatever the
+  // logits hold; it is clamped all the same, as an id outside would address memory outside the
+  // weight stack
+  const int e = min(max(*pick, 0), E - 1);
 
   // 2. 16 rows (gate rows j..j+7 and the matching up rows) and a part of K per wavefront
   const int part = wave % ksplit;
@@ -231,7 +234,7 @@ decode_gate_up_kernel(const float* __restrict__ logits, const uint16_t* __restri
 
 template <int SEG>
 __global__ void __launch_bounds__(kDecMaxThreads)
-decode_down_kernel(const uint16_t* __restrict__ h, int k, const int32_t* __restrict__ ids,
+decode_down_kernel(const uint16_t* __restrict__ h, int E, int k, const int32_t* __restrict__ ids,
                    const float* __restrict__ w, const uint8_t* __restrict__ q,
                    const uint8_t* __restrict__ s, const float* __restrict__ bias, int D, int F,
                    int ksplit, float* __restrict__ d, float* __restrict__ y) {
@@ -249,7 +252,8 @@ decode_down_kernel(const uint16_t* __restrict__ h, int k, const int32_t* __restr
   // from the copy: the weights go out as soon as it arrives (a vector load of it was waited for
   // together with the whole copy, whose trip count the compiler does not know)
   const int slot = __builtin_amdgcn_readfirstlane(wave / ksplit), part = wave % ksplit;
-  const int e = ((const __attribute__((address_space(4))) int32_t*)ids)[t * k + slot];
+  const int e = min(max(((const __attribute__((address_space(4))) int32_t*)ids)[t * k + slot], 0),
+                    E - 1);   // in [0, E) by the routing; clamped as in launch 1
   lds_dma_copy(h + (size_t)t * k * F, (uint32_t)k * row_bytes, xs, wave, nthreads >> 6);
   __builtin_amdgcn_sched_barrier(0);
   int cb, ce, Cp;
@@ -370,6 +374,8 @@ __device__ __forceinline__ void down_item_persistent(
     e = __shfl(my_id, slot);
     if (wave == 0) wsl = topk_weight(my_v, k);
   }
+
+  e = min(max(e, 0), E - 1);   // in [0, E) by the total order; clamped as in gate_up_item
 
   // 2. this wavefront's down rows in flight before the wait
   int cb, ce, Cp;
@@ -565,7 +571,7 @@ extern "C" int mx4_moe_decode(const float* logits, const uint16_t* x, int64_t T,
               basep, row_tok, pos, h);
   if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
   const dim3 g2((unsigned)((D + 15) / 16), (unsigned)T);
-  moe::launch(moe::decode_down_kernel<moe::kGvSeg>, g2, dim3(64 * waves2), lds2, st, h, k, ids, w,
+  moe::launch(moe::decode_down_kernel<moe::kGvSeg>, g2, dim3(64 * waves2), lds2, st, h, E, k, ids, w,
               w_dn->q, w_dn->s, w_dn->bias, D, F, ks2, d, y);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

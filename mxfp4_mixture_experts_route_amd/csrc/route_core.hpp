@@ -14,9 +14,14 @@ namespace moe {
 
 constexpr int kRoutePerLane = MOE_MAX_E / kWave;     // logits held per lane
 
-// a ranks before b: larger value; ties -> lower id. -0.0 == +0.0 as floats.
+// a ranks before b in a total order of (value, id): a number before a NaN (a NaN logit ranks
+// below every number, -inf included), the larger number first, equal values (-0.0 == +0.0) and
+// two NaNs by the lower id. Being total, it gives every logit of a row a distinct rank, so the
+// first k ranks always name k distinct experts in [0, E), whatever the row holds.
 __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-  return (va > vb) || (va == vb && ia < ib);
+  const bool na = va != va, nb = vb != vb;
+  const bool lower_id = ia < ib;
+  return (nb & (!na | lower_id)) | (!na & !nb & ((va > vb) | ((va == vb) & lower_id)));
 }
 
 // Logits of one row for wave_topk_select: lane l holds experts j*64 + l (0 past E).
@@ -141,9 +146,6 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
   wave_topk_select(v, E, k, my_id, my_v);
 }
 
-// Routing weights of the picks held by lanes 0..k-1 (wave_topk): lane 0 sums exp(v_r - v_0) in
-// double in pick order, then writes ids[r] and w[r] = f32(exp(v_r - v_0) / sum) for r < k.
-// Every lane must call it (it shuffles).
 // Routing weight of the pick held by this lane (lanes 0..k-1 of wave_topk): the softmax over the
 // k picks, summed in double in pick order relative to pick 0, rounded to f32. Every lane must
 // call it (it shuffles); lanes >= k get a value of no meaning.

@@ -30,13 +30,15 @@ logits; the clamped SwiGLU with alpha = 1.702 and limit = 7).
 Readings where the pages are silent (each pinned in tests/test_oracle_pins.py):
   - element 2i of a row is the low nibble of byte i, element 2i+1 the high nibble;
   - e8m0 byte 255 decodes to NaN; a decoded weight beyond the fp32 range is +-inf;
-  - top-k ties go to the lower expert id; weights = softmax of the k selected logits in double,
-    rounded to f32;
+  - top-k ties go to the lower expert id, and a NaN logit ranks below every number (a total
+    order); weights = softmax of the k selected logits in double, rounded to f32;
   - CSR rows within a bucket are in ascending token order; padding/ghost rows hold -1;
   - gate_up rows [0, F) are the gate, rows [F, 2F) the up projection;
   - the router is a linear layer with bias over bf16 rows ([ext, gpt-oss]), bf16 weights;
   - MXFP8 activations (the MX-scaled MFMA variant; [ext] OCP 8-bit FP and MX v1.0): an all-zero
-    block takes the smallest scale; elements round to nearest even and saturate at 448.
+    block takes the smallest scale; elements round to nearest even and saturate at 448; the
+    projection is the MX dot product (each block's exact sum scaled, result stored as fp32), so
+    a zero activation times a weight beyond the fp32 range contributes 0.
 
 Every function is pinned (closed forms, invariants, brute force, exact arithmetic); none is
 "parity unpinned".
@@ -59,7 +61,8 @@ E2M1_TABLE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
 
 def e2m1_decode(codes) -> np.ndarray:
     """Value of each 4-bit e2m1 code ([mx4] 16-value table; [ext] OCP MX v1.0)."""
-    return E2M1_TABLE[np.asarray(codes, dtype=np.int64)]
+    codes = np.asarray(codes)
+    return E2M1_TABLE[codes if codes.dtype == np.uint8 else codes.astype(np.int64)]
 
 
 def e8m0_decode(e) -> np.ndarray:
@@ -82,16 +85,23 @@ def unpack_codes(q: np.ndarray) -> np.ndarray:
     return codes
 
 
-def dequant(q: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """Decoded MXFP4 matrix [..., N, K] as fp32 values: e2m1(code) * 2^(s-127) for the 32-element
-    block holding the element ([mx4]). The product is exact in float64 and is then stored as an
-    fp32 value, which overflows to +-inf beyond the fp32 range (reading)."""
+def dequant_exact(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Decoded MXFP4 matrix [..., N, K] as exact float64 values: e2m1(code) * 2^(s-127) for the
+    32-element block holding the element ([mx4]); NaN where the scale byte is 255. A float64
+    holds every such product exactly (2 significant bits, exponents -128..130)."""
     codes = unpack_codes(q)
     K = codes.shape[-1]
     scale = np.repeat(e8m0_decode(s), 32, axis=-1)
     assert scale.shape[-1] == K
+    return e2m1_decode(codes) * scale
+
+
+def dequant(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Decoded MXFP4 matrix [..., N, K] as fp32 values, the operand of the bf16-activation
+    projections: dequant_exact's values stored as fp32, which overflows to +-inf beyond the fp32
+    range (reading; in range the value is exact in fp32 and in bf16 alike)."""
     with np.errstate(over="ignore", invalid="ignore"):
-        return (e2m1_decode(codes) * scale).astype(np.float32)
+        return dequant_exact(q, s).astype(np.float32)
 
 
 # --------------------------------------------------------------------------------------------
@@ -203,13 +213,29 @@ def router_logits(x_bits, w_bits, bias=None) -> np.ndarray:
     return b[None, :] + x @ W.T, np.abs(b)[None, :] + np.abs(x) @ np.abs(W).T
 
 
+def _beats(a: float, b: float) -> bool:
+    """Logit a ranks strictly above logit b: a number above a NaN, else the larger number."""
+    if math.isnan(a) or math.isnan(b):
+        return math.isnan(b) and not math.isnan(a)
+    return a > b
+
+
+def _exp(v: float) -> float:
+    """e^v, NaN for NaN (math.exp raises on nothing here: v <= 0 or NaN)."""
+    return math.nan if math.isnan(v) else math.exp(v)
+
+
 def route_topk(logits: np.ndarray, k: int):
     """Top-k routing of each token.
 
     ids: the k largest logits, descending; equal logits ordered by ascending expert id
     ([chain] names per-token expert ids; [mx4] k = 4 at gpt-oss shape; tie order is a reading).
+    A NaN logit ranks below every number, -inf included, and NaNs among themselves by id
+    (reading: the pages route finite logits; this makes the order total, so any row yields k
+    distinct experts).
     w: softmax over the k selected logits [ext, gpt-oss router], w_s = exp(l_s - l_0) /
-    sum_j exp(l_j - l_0) in float64, summed in slot order, rounded to f32.
+    sum_j exp(l_j - l_0) in float64, summed in slot order, rounded to f32 (NaN wherever a NaN
+    logit enters the sum).
     """
     logits = np.asarray(logits, dtype=np.float32)
     T, E = logits.shape
@@ -222,13 +248,13 @@ def route_topk(logits: np.ndarray, k: int):
         for _ in range(k):
             best = remaining[0]
             for e in remaining[1:]:
-                if float(logits[t, e]) > float(logits[t, best]):   # strict: ties keep lower id
+                if _beats(float(logits[t, e]), float(logits[t, best])):  # strict: ties keep lower id
                     best = e
             chosen.append(best)
             remaining.remove(best)
         ids[t] = chosen
         l0 = float(logits[t, chosen[0]])
-        num = [math.exp(float(logits[t, e]) - l0) for e in chosen]
+        num = [_exp(float(logits[t, e]) - l0) for e in chosen]
         den = 0.0
         for v in num:
             den += v
@@ -301,16 +327,42 @@ def project(a_bits, a_row, q, s, bias, counts, basep, mpad: int):
     return project_values(bf16_to_f64(a_bits), a_row, q, s, bias, counts, basep, mpad)
 
 
+# Smallest magnitude that an fp32 store rounds (to nearest even) to infinity: halfway between
+# the largest finite fp32 value (2 - 2^-23) * 2^127 and 2^128.
+FP32_OVERFLOW = (2.0 - 2.0 ** -24) * 2.0 ** 127
+
+
+def round_fp32_range(v: np.ndarray) -> np.ndarray:
+    """float64 values as an fp32 result holds them in range: magnitudes at or beyond
+    FP32_OVERFLOW become +-inf; everything else is left at float64 precision (the tolerance
+    covers the fp32 rounding)."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(invalid="ignore"):
+        return np.where(np.abs(v) >= FP32_OVERFLOW, np.copysign(np.inf, v), v)
+
+
 def project_mx8(a_codes, a_scales, a_row, q, s, bias, counts, basep, mpad: int):
     """The projection of `project` with MXFP8 activation rows (codes [rows][K], scales
     [rows][K/32], as mx8_quantize returns them) in place of bf16 rows: x_r is the exact value of
-    the quantized row, and everything else is unchanged."""
-    return project_values(mx8_dequant(a_codes, a_scales), a_row, q, s, bias, counts, basep,
-                          mpad)
+    the quantized row.
+
+    The product follows the OCP MX v1.0 dot product [ext]: each pair of 32-value blocks
+    contributes its exact sum of element products times the two blocks' scales, and the result
+    is stored as fp32. So the weights are taken at their exact values (dequant_exact: a decoded
+    weight beyond the fp32 range is a finite number here, and a zero activation times it is
+    0), every product x_i * w_i is exact in float64, the sum rounds at float64, and the result
+    is rounded into the fp32 range (round_fp32_range). A block with scale byte 255 is NaN, and
+    so is every output it enters. Partial sums that would overflow fp32 on the way are not
+    modelled (no test input reaches the fp32 range except through a single block)."""
+    out, S = project_values(mx8_dequant(a_codes, a_scales), a_row, q, s, bias, counts, basep,
+                            mpad, weights=dequant_exact)
+    return round_fp32_range(out), S
 
 
-def project_values(a, a_row, q, s, bias, counts, basep, mpad: int):
-    """The projection of `project` with the activation rows given as float64 values [rows][K]."""
+def project_values(a, a_row, q, s, bias, counts, basep, mpad: int, weights=None):
+    """The projection of `project` with the activation rows given as float64 values [rows][K]
+    and the weights decoded by `weights` (default: dequant, fp32 values)."""
+    weights = dequant if weights is None else weights
     E, N, _ = q.shape
     K = q.shape[2] * 2
     out = np.full((mpad, N), np.nan, dtype=np.float64)
@@ -322,7 +374,7 @@ def project_values(a, a_row, q, s, bias, counts, basep, mpad: int):
         rows = int(basep[e]) + np.arange(c)
         src = rows if a_row is None else np.asarray(a_row)[rows]
         x = a[src]                                                  # [c][K]
-        W = dequant(q[e], s[e]).astype(np.float64)                  # [N][K]
+        W = weights(q[e], s[e]).astype(np.float64)                  # [N][K]
         b = np.zeros(N) if bias is None else np.asarray(bias[e], dtype=np.float64)
         with np.errstate(invalid="ignore", over="ignore"):
             out[rows] = b[None, :] + x @ W.T
@@ -333,19 +385,20 @@ def project_values(a, a_row, q, s, bias, counts, basep, mpad: int):
 
 def project_at(a_bits, a_row, q, s, bias, counts, basep, samples):
     """The same projection as `project`, evaluated only at the sampled (row, n) pairs (rows must
-    be live). For full-size checks where the whole product is too slow on the CPU."""
+    be live). For checks of single outputs where the whole product is not needed."""
     a = np.asarray(a_bits)
     return _project_at(lambda src: bf16_to_f64(a[src]), a_row, q, s, bias, counts, basep,
-                       samples)
+                       samples, dequant)
 
 
 def project_mx8_at(a_codes, a_scales, a_row, q, s, bias, counts, basep, samples):
     """project_mx8 evaluated only at the sampled (row, n) pairs (rows must be live)."""
-    return _project_at(lambda src: mx8_dequant(a_codes[src], a_scales[src]), a_row, q, s, bias,
-                       counts, basep, samples)
+    vals, S = _project_at(lambda src: mx8_dequant(a_codes[src], a_scales[src]), a_row, q, s,
+                          bias, counts, basep, samples, dequant_exact)
+    return round_fp32_range(vals), S
 
 
-def _project_at(row_values, a_row, q, s, bias, counts, basep, samples):
+def _project_at(row_values, a_row, q, s, bias, counts, basep, samples, weights):
     basep = np.asarray(basep)
     counts = np.asarray(counts)
     vals = np.empty(len(samples), dtype=np.float64)
@@ -355,7 +408,7 @@ def _project_at(row_values, a_row, q, s, bias, counts, basep, samples):
         assert basep[e] <= r < basep[e] + counts[e], "sampled row is not live"
         src = r if a_row is None else int(a_row[r])
         x = row_values(src)
-        w = dequant(q[e, n][None, :], s[e, n][None, :])[0].astype(np.float64)
+        w = weights(q[e, n][None, :], s[e, n][None, :])[0].astype(np.float64)
         b = 0.0 if bias is None else float(bias[e, n])
         with np.errstate(invalid="ignore", over="ignore"):
             vals[i] = b + float(np.dot(x, w))

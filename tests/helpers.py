@@ -87,3 +87,22 @@ def live_mask(counts, basep, mpad):
     for e in range(len(counts)):
         m[basep[e]:basep[e] + counts[e]] = True
     return m
+
+
+def assert_swiglu_within(h_bits, g_ref, S_g, F, what, alpha, limit):
+    """bf16 h from a fused gate_up epilogue (no fp32 intermediate to stage from) against the
+    SwiGLU-OAI of the oracle's own gate_up rows g_ref [rows][2F]: within one bf16 ulp of the
+    exact activation plus the gate_up tolerance carried through it (|dh/dgate| <= 1.1*(|uc|+1)
+    <= 8.8 and |dh/dup| <= limit where the input is not clamped)."""
+    g_ref = np.asarray(g_ref, dtype=np.float64)
+    S_g = np.asarray(S_g, dtype=np.float64)
+    tol_g = REL_TOL * S_g[:, :F] + ABS_TOL
+    tol_u = REL_TOL * S_g[:, F:] + ABS_TOL
+    ref = oracle.swiglu_oai(g_ref, alpha, limit)
+    got = oracle.bf16_to_f64(h_bits)
+    bound = bf16_ulp(oracle.bf16_round(ref)) + 8.8 * tol_g + limit * tol_u
+    ok = np.abs(got - ref) <= bound
+    if not np.all(ok):
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} outside; first at {i}: "
+                             f"got={got[i]} ref={ref[i]} bound={bound[i]}")

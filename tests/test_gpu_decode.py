@@ -73,7 +73,10 @@ def run_and_check(c, against_csr=True):
 
     ids_ref, w_ref = oracle.route_topk(c["logits"], k)
     assert np.array_equal(host(out["ids"]), ids_ref)
-    assert np.array_equal(host(out["w"]).view(np.uint32), w_ref.view(np.uint32))
+    w_got = host(out["w"])   # bit for bit; a NaN weight (NaN logits) meets a NaN of any payload
+    assert np.array_equal(np.isnan(w_got), np.isnan(w_ref))
+    assert np.array_equal(np.where(np.isnan(w_got), 0, w_got).view(np.uint32),
+                          np.where(np.isnan(w_ref), 0, w_ref).astype(np.float32).view(np.uint32))
     mpad = T * k
     cnt, bp, rt, pos = oracle.bucket(ids_ref, E, 1, mpad)
     for nm, ref in (("counts", cnt), ("basep", bp), ("row_tok", rt), ("pos", pos)):
@@ -135,9 +138,25 @@ def test_decode_ties_route_like_route_topk():
     run_and_check(c)
 
 
+@pytest.mark.parametrize("E", [32, 128])
+def test_decode_nan_logits_route_in_range(E):
+    """A token whose logits row is NaN (all or part) routes to k distinct experts in [0, E), the
+    oracle's order; the fused kernels then stream those experts' rows (finite x, so h, d and y
+    are finite and within tolerance)."""
+    c = make_case(31 + E, E=E, D=64, F=64, T=4, k=4)
+    c["logits"][0] = np.nan
+    c["logits"][1, ::3] = np.nan
+    c["logits"][2] = -np.inf
+    log(f"decode NaN logits E={E}")
+    out = run_and_check(c, against_csr=False)
+    ids = host(out["ids"])
+    assert ids.min() >= 0 and ids.max() < E
+
+
+@pytest.mark.timeout(600)
 def test_decode_full_size_gptoss_t1():
-    """The bench's decode layer (gpt-oss-20b shape, T = 1), sampled against the oracle and whole
-    against the five-call chain."""
+    """The bench's decode layer (gpt-oss-20b shape, T = 1) against the oracle on every output,
+    and whole against the five-call chain."""
     wl = synth.WORKLOADS["decode_t1"]
     tok = synth.tokens(wl, 0)
     W = synth.layer_weights(wl, 0)
@@ -153,26 +172,18 @@ def test_decode_full_size_gptoss_t1():
     for nm, ref in (("counts", cnt), ("basep", bp), ("row_tok", rt), ("pos", pos)):
         assert np.array_equal(host(out[nm]), ref), nm
     pos_flat = pos.reshape(-1)
-    rng = np.random.default_rng(5)
     h_bits = bf16_host(out["h"])
-    # sampled gate_up rows through SwiGLU: (routed row, j) -> CSR rows of gate j and up F + j
-    rho = rng.integers(0, wl.k, 256)
-    js = rng.integers(0, wl.ffn, 256)
-    samples = [(pos_flat[r], j) for r, j in zip(rho, js)] + \
-              [(pos_flat[r], wl.ffn + j) for r, j in zip(rho, js)]
-    g, S = oracle.project_at(tok["x"], rt, W["gate_up"]["q"], W["gate_up"]["s"],
-                             W["gate_up"]["bias"], cnt, bp, samples)
-    g2 = np.concatenate([g[:256, None], g[256:, None]], axis=1)
-    S2 = np.concatenate([S[:256, None], S[256:, None]], axis=1)
-    check_h(h_bits[rho, js][:, None], g2, S2, np.arange(256), 1, "full-size fused h")
-    # d from the GPU's h, sampled
+    # every h value against the activation of the oracle's gate_up rows
+    g_ref, S_g = oracle.project(tok["x"], rt, W["gate_up"]["q"], W["gate_up"]["s"],
+                                W["gate_up"]["bias"], cnt, bp, wl.k)
+    check_h(h_bits, g_ref, S_g, pos_flat, wl.ffn, "full-size fused h")
+    # every d value from the GPU's h
     h_csr = np.zeros_like(h_bits)
     h_csr[pos_flat] = h_bits
-    ns = rng.integers(0, wl.dim, 256)
-    d_ref, d_S = oracle.project_at(h_csr, None, W["down"]["q"], W["down"]["s"], W["down"]["bias"],
-                                   cnt, bp, [(pos_flat[r], n) for r, n in zip(rho, ns)])
+    d_ref, d_S = oracle.project(h_csr, None, W["down"]["q"], W["down"]["s"], W["down"]["bias"],
+                                cnt, bp, wl.k)
     d_h = host(out["d"])
-    assert_within(d_h[rho, ns], d_ref, d_S, "full-size fused d")
+    assert_within(d_h, d_ref[pos_flat], d_S[pos_flat], "full-size fused d")
     y_ref, y_S = oracle.combine(d_h, np.arange(wl.k, dtype=np.int32).reshape(1, wl.k), w_ref)
     assert_within(host(out["y"]), y_ref, y_S, "full-size fused y")
     ref = moe.moe_layer(x_d, logits_d, GU, DN, wl.k, 1, ALPHA, LIMIT, projection="gemv")

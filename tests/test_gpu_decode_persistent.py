@@ -102,9 +102,11 @@ def test_persistent_workspace_reused_and_deterministic():
         assert np.array_equal(host(a[key]).view(np.uint32), host(c2[key]).view(np.uint32)), key
 
 
+@pytest.mark.timeout(600)
 def test_persistent_full_size_gptoss_t1():
-    """The bench's decode layer (gpt-oss-20b shape, T = 1): routing exact, y against the oracle
-    combine of the GPU's d, sampled d against the oracle from the GPU's h."""
+    """The bench's decode layer (gpt-oss-20b shape, T = 1): routing exact; every h value
+    against the activation of the oracle's gate_up rows, every d value against the oracle from
+    the GPU's h, y against the oracle combine of the GPU's d."""
     wl = synth.WORKLOADS["decode_t1"]
     tok = synth.tokens(wl, 0)
     W = synth.layer_weights(wl, 0)
@@ -116,23 +118,15 @@ def test_persistent_full_size_gptoss_t1():
     assert np.array_equal(host(out["ids"]), ids_ref)
     cnt, bp, rt, pos = oracle.bucket(ids_ref, wl.E, 1, wl.k)
     pos_flat = pos.reshape(-1)
-    rng = np.random.default_rng(9)
     h_bits = bf16_host(out["h"])
-    rho = rng.integers(0, wl.k, 256)
-    js = rng.integers(0, wl.ffn, 256)
-    samples = [(pos_flat[r], j) for r, j in zip(rho, js)] + \
-              [(pos_flat[r], wl.ffn + j) for r, j in zip(rho, js)]
-    g, S = oracle.project_at(tok["x"], rt, W["gate_up"]["q"], W["gate_up"]["s"],
-                             W["gate_up"]["bias"], cnt, bp, samples)
-    g2 = np.concatenate([g[:256, None], g[256:, None]], axis=1)
-    S2 = np.concatenate([S[:256, None], S[256:, None]], axis=1)
-    check_h(h_bits[rho, js][:, None], g2, S2, np.arange(256), 1, "full-size persistent h")
+    g_ref, S_g = oracle.project(tok["x"], rt, W["gate_up"]["q"], W["gate_up"]["s"],
+                                W["gate_up"]["bias"], cnt, bp, wl.k)
+    check_h(h_bits, g_ref, S_g, pos_flat, wl.ffn, "full-size persistent h")
     h_csr = np.zeros_like(h_bits)
     h_csr[pos_flat] = h_bits
-    ns = rng.integers(0, wl.dim, 256)
-    d_ref, d_S = oracle.project_at(h_csr, None, W["down"]["q"], W["down"]["s"], W["down"]["bias"],
-                                   cnt, bp, [(pos_flat[r], n) for r, n in zip(rho, ns)])
+    d_ref, d_S = oracle.project(h_csr, None, W["down"]["q"], W["down"]["s"], W["down"]["bias"],
+                                cnt, bp, wl.k)
     d_h = host(out["d"])
-    assert_within(d_h[rho, ns], d_ref, d_S, "full-size persistent d")
+    assert_within(d_h, d_ref[pos_flat], d_S[pos_flat], "full-size persistent d")
     y_ref, y_S = oracle.combine(d_h, np.arange(wl.k, dtype=np.int32).reshape(1, wl.k), w_ref)
     assert_within(host(out["y"]), y_ref, y_S, "full-size persistent y")

@@ -153,6 +153,29 @@ def test_route_ties_and_signed_zero():
         assert np.array_equal(host(w), w_ref)
 
 
+@pytest.mark.parametrize("E,k", [(32, 4), (64, 8), (100, 4), (1024, 16)])
+def test_route_nan_rows_give_experts_in_range(E, k):
+    """NaN logits rank below every number (a total order): rows with NaNs, all-NaN rows and
+    -inf route to k distinct ids in [0, E), bit for bit the oracle's; both rank paths (E <= 64
+    and the arg-best rounds past 64)."""
+    g = np.random.default_rng(E + k)
+    logits = (np.round(g.standard_normal((24, E)) * 2) / 2).astype(np.float32)
+    logits[g.random((24, E)) < 0.4] = np.nan
+    logits[g.random((24, E)) < 0.05] = -np.inf
+    logits[0] = np.nan
+    logits[1, :] = -np.inf
+    logits[2, : E // 2] = np.nan
+    log(f"route NaN rows E={E} k={k}")
+    ids, w = moe.moe_route_topk(dev(logits), k)
+    ids_ref, w_ref = oracle.route_topk(logits, k)
+    got = host(ids)
+    assert got.min() >= 0 and got.max() < E
+    assert np.array_equal(got, ids_ref)
+    wg = host(w)
+    assert np.array_equal(np.isnan(wg), np.isnan(w_ref))
+    assert np.array_equal(np.nan_to_num(wg), np.nan_to_num(w_ref))
+
+
 # ---------------------------------------------------------------------------------------------
 # staged projections on a case that spans several tiles with ragged tails
 # ---------------------------------------------------------------------------------------------

@@ -142,3 +142,81 @@ def test_project_mx8_equals_bf16_projection_when_quantization_is_lossless():
     v, vS = oracle.project_mx8_at(xq, xs, row_tok, W["q"], W["s"], W["bias"], counts, basep,
                                   samples)
     assert np.array_equal(v, np.array([a[r, n] for r, n in samples]))
+
+
+def _one_block_case(w_code, w_scale, x_val):
+    """One expert, one output row, K = 32: weight block of one code at element 0 with the given
+    scale byte, activation row with x_val at element 0 (quantized exactly)."""
+    q = np.zeros((1, 1, 16), dtype=np.uint8)
+    q[0, 0, 0] = w_code
+    s = np.full((1, 1, 1), w_scale, dtype=np.uint8)
+    x = np.zeros((1, 32))
+    x[0, 0] = x_val
+    xq, xs = oracle.mx8_quantize(_bf16(x))
+    counts, basep = np.array([1]), np.array([0, 1])
+    return oracle.project_mx8(xq, xs, None, q, s, None, counts, basep, 1)
+
+
+def test_project_mx8_scales_the_exact_block_sum():
+    # OCP MX dot product: a zero activation times a weight beyond the fp32 range (code 7 = 6.0
+    # at scale byte 254: 6 * 2^127) contributes 0, not 0 * inf
+    out, S = _one_block_case(7, 254, 0.0)
+    assert out[0, 0] == 0.0 and S[0, 0] == 0.0
+    # activated, the same weight is beyond the fp32 range: the fp32 result is +inf (-inf for
+    # code 15 = -6.0); 1.5 * 2^127 (code 3) is finite and exact
+    assert _one_block_case(7, 254, 1.0)[0][0, 0] == np.inf
+    assert _one_block_case(15, 254, 1.0)[0][0, 0] == -np.inf
+    assert _one_block_case(3, 254, 1.0)[0][0, 0] == 1.5 * 2.0 ** 127
+    assert _one_block_case(7, 253, -1.0)[0][0, 0] == -np.inf        # 6 * 2^126 = 1.5 * 2^128
+    # scale byte 255 is NaN: the block is NaN whatever the activation
+    assert np.isnan(_one_block_case(2, 255, 0.0)[0][0, 0])
+    assert np.isnan(_one_block_case(2, 255, 1.0)[0][0, 0])
+
+
+def test_round_fp32_range_threshold():
+    # the largest finite fp32 stays; halfway to 2^128 rounds (to even) to inf
+    big = float(np.finfo(np.float32).max)
+    half = oracle.FP32_OVERFLOW
+    assert np.float32(half) == np.inf and np.float32(np.nextafter(half, 0)) == big
+    v = oracle.round_fp32_range(np.array([big, -big, half, -half, np.nextafter(half, 0), 1.0]))
+    assert v.tolist() == [big, -big, np.inf, -np.inf, np.nextafter(half, 0), 1.0]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_project_mx8_exact_rational_brute_force(seed):
+    # small case with scales across the whole e8m0 range (product terms beyond the fp32 range
+    # included): the oracle equals the exact rational sum of the block terms, rounded to
+    # float64 and then into the fp32 range, within the float64 summation error
+    from fractions import Fraction
+    g = np.random.default_rng(seed + 40)
+    N, K, T = 6, 96, 3
+    q = g.integers(0, 256, (1, N, K // 2)).astype(np.uint8)
+    s = g.integers(100, 255, (1, N, K // 32)).astype(np.uint8)
+    x = g.standard_normal((T, K)) * np.exp2(g.integers(-8, 8, (T, K)))
+    xq, xs = oracle.mx8_quantize(_bf16(x))
+    bias = g.standard_normal((1, N)).astype(np.float32)
+    counts, basep = np.array([T]), np.array([0, T])
+    out, S = oracle.project_mx8(xq, xs, None, q, s, bias, counts, basep, T)
+    codes = oracle.unpack_codes(q[0])
+    e2m1 = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+            Fraction(4), Fraction(6)]
+    for r in range(T):
+        for n in range(N):
+            tot = Fraction(float(bias[0, n]))
+            mag = abs(tot)
+            for b in range(K // 32):
+                blk = Fraction(0)
+                for i in range(32 * b, 32 * b + 32):
+                    c = int(codes[n, i])
+                    wv = -e2m1[c & 7] if c & 8 else e2m1[c & 7]
+                    blk += Fraction(float(oracle.e4m3_decode(xq[r, i]))) * wv
+                    mag += abs(Fraction(float(oracle.e4m3_decode(xq[r, i]))) * wv) * \
+                        Fraction(2) ** (int(xs[r, b]) - 127) * Fraction(2) ** (int(s[0, n, b]) - 127)
+                tot += blk * Fraction(2) ** (int(xs[r, b]) - 127) * Fraction(2) ** (int(s[0, n, b]) - 127)
+            exact = float(tot)
+            expect = oracle.round_fp32_range(np.array([exact]))[0]
+            if np.isinf(expect):
+                assert out[r, n] == expect
+            else:
+                assert abs(out[r, n] - exact) <= 1e-13 * float(mag) + 1e-300, (r, n)
+            assert abs(S[r, n] - float(mag)) <= 1e-13 * float(mag)

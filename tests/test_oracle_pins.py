@@ -144,6 +144,35 @@ def test_route_hand_cases():
     assert ids.tolist() == [[1, 2]]
 
 
+def test_route_nan_logits_total_order():
+    # reading: a NaN logit ranks below every number (-inf included), NaNs among themselves by
+    # id, so every row yields k distinct experts in [0, E); weights are NaN where a NaN enters
+    nan, inf = float("nan"), float("inf")
+    ids, w = oracle.route_topk(np.array([[nan, 1.0, nan, 2.0]], dtype=np.float32), 4)
+    assert ids.tolist() == [[3, 1, 0, 2]]
+    assert np.all(np.isnan(w[0, 2:]))
+    ids, w = oracle.route_topk(np.array([[nan, 1.0, nan, 2.0]], dtype=np.float32), 2)
+    assert ids.tolist() == [[3, 1]] and np.all(np.isfinite(w))
+    ids, w = oracle.route_topk(np.full((2, 32), np.nan, dtype=np.float32), 4)
+    assert ids.tolist() == [[0, 1, 2, 3]] * 2 and np.all(np.isnan(w))
+    ids, _ = oracle.route_topk(np.array([[nan, -inf, nan, -inf]], dtype=np.float32), 3)
+    assert ids.tolist() == [[1, 3, 0]]
+
+
+@pytest.mark.parametrize("E,k,seed", [(8, 4, 10), (32, 4, 11), (100, 8, 12)])
+def test_route_nan_rows_against_sort(E, k, seed):
+    # brute force: a full sort by the key (is NaN, -value, id)
+    g = np.random.default_rng(seed)
+    logits = (np.round(g.standard_normal((30, E)) * 2) / 2).astype(np.float32)
+    logits[g.random((30, E)) < 0.3] = np.nan
+    logits[g.random((30, E)) < 0.05] = -np.inf
+    logits[0] = np.nan
+    ids, _ = oracle.route_topk(logits, k)
+    for t in range(logits.shape[0]):
+        key = lambda e: (math.isnan(logits[t, e]), 0.0 if math.isnan(logits[t, e]) else -float(logits[t, e]), e)
+        assert ids[t].tolist() == sorted(range(E), key=key)[:k]
+
+
 def test_route_two_experts_closed_form():
     # k=2 softmax: w1 = 1 / (1 + e^(l0 - l1)); with l0 - l1 = ln 3, w = (3/4, 1/4) exactly
     l0 = np.float32(0.5)
