@@ -20,7 +20,7 @@ MOE_MAX_K, MOE_MAX_E, MOE_MAX_TILE_M = 16, 1024, 256
 EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_pack_experts",
            "mx4_moe_gemv", "mx4_moe_gemm", "moe_combine", "mx4_moe_decode", "moe_timing_arm",
            "moe_timing_read", "mx8_quantize", "mx4_moe_gemm_mx8", "moe_router",
-           "mx4_moe_decode_persistent")
+           "mx4_moe_decode_persistent", "moe_probe_read", "moe_probe_mfma_bf16")
 MOE_DECODE_WS_WORDS = 32
 MOE_ROUTER_MAX_ROUTED = 16384
 MOE_MX8_GEMM_MAX_K = 4096
@@ -90,6 +90,10 @@ def lib() -> ctypes.CDLL:
         L.mx4_moe_gemm_mx8.restype = ci
         L.mx4_moe_gemm_mx8.argtypes = [vp, vp, vp, i64, ctypes.POINTER(Mx4ExpertsC), vp, vp, ci,
                                        i64, ci, cf, cf, vp, vp, vp]
+        L.moe_probe_read.restype = ci
+        L.moe_probe_read.argtypes = [vp, i64, vp, ci, vp]
+        L.moe_probe_mfma_bf16.restype = ci
+        L.moe_probe_mfma_bf16.argtypes = [ci, ci, vp, vp]
         _lib = L
     return _lib
 
@@ -457,3 +461,26 @@ def moe_layer(x, logits, gate_up: MX4Experts, down: MX4Experts, k: int, tile_m: 
     y = moe_combine(d, pos, w, stream=stream)
     return {"ids": ids, "w": w, "mpad": mpad, "counts": counts, "basep": basep,
             "row_tok": row_tok, "pos": pos, "h": h, "d": d, "y": y, **extra}
+
+
+# ---------------------------------------------------------------------------------------------
+# attained-peak probes (measurement only)
+# ---------------------------------------------------------------------------------------------
+
+def moe_probe_read(buf, workgroups: int, sink=None, stream=None):
+    """Read every byte of the device tensor `buf` once (moe_probe_read); returns the sink."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _call("moe_probe_read", _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+          int(workgroups), _stream(stream))
+    return sink
+
+
+def moe_probe_mfma_bf16(workgroups: int, iters: int, sink=None, stream=None):
+    """workgroups * 4 * iters * 8 bf16 MFMAs of 16384 flops each (moe_probe_mfma_bf16)."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    _call("moe_probe_mfma_bf16", int(workgroups), int(iters), _ptr(sink), _stream(stream))
+    return sink

@@ -23,7 +23,7 @@ ARCH = "gfx950"
 
 SOURCES = ["capi.hip", "pack.hip", "route.hip", "bucket.hip", "gemv.hip", "gemm.hip", "combine.hip",
            "decode.hip", "timing.hip", "quant.hip",
-           "router.hip"]
+           "router.hip", "probe.hip"]
 
 # -packed-fp32-ops: no packed fp32 VALU ops (v_pk_fma_f32 and friends) anywhere in device code.
 CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",

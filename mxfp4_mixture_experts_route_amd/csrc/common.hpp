@@ -135,18 +135,23 @@ __device__ __forceinline__ float mx8_inv_scale(uint32_t sbyte) {
 
 // Clamped SwiGLU-OAI of one (gate, up) pair: gc = min(gate, limit), uc = clamp(up, +-limit),
 // gc * sigmoid(alpha*gc) * (uc + 1). The sigmoid is evaluated on the side where the exponential
-// cannot overflow (e = exp(-|z|) <= 1), so very negative gates give correctly tiny (not
-// zero-by-overflow) results. exp(-|z|) = 2^(-|z| log2 e) and 1 / (1 + e) use the hardware's
-// exp2 and reciprocal (about 1 ulp each, far below the bf16 rounding of h); the accurate library
-// exp and IEEE division cost ~40 VALU ops per value in epilogues that run while HBM idles.
+// cannot overflow (e = exp(-|z|) <= 1). exp(-|z|) = 2^(-|z| log2 e) and 1 / (1 + e) use the
+// hardware's exp2 and reciprocal (about 1 ulp each, far below the bf16 rounding of h); the
+// accurate library exp and IEEE division cost ~40 VALU ops per value in epilogues that run
+// while HBM idles. The hardware exp2 returns 0 below the normal range (2^-126), which for very
+// negative gates (|z| beyond ~87) would zero an h that bf16 still represents (its smallest
+// magnitude is 2^-133): there the exponent is taken 64 higher, exactly (|z| log2 e >= 64 has
+// no bits below 2^-17), and the product is scaled back by 2^-64 at the end.
 __device__ __forceinline__ float swiglu_oai(float gate, float up, float alpha, float limit) {
   const float gc = fminf(gate, limit);
   const float uc = fminf(fmaxf(up, -limit), limit);
   const float z = alpha * gc;
-  const float ez = __builtin_amdgcn_exp2f(-fabsf(z) * 1.44269504088896341f);
-  const float r = __builtin_amdgcn_rcpf(1.0f + ez);
-  const float sig = (z >= 0.0f) ? r : ez * r;
-  return gc * sig * (uc + 1.0f);
+  const float x = -fabsf(z) * 1.44269504088896341f;
+  const bool tiny = x < -64.0f;                                   // e < 2^-64
+  const float es = __builtin_amdgcn_exp2f(tiny ? x + 64.0f : x);  // e, times 2^64 when tiny
+  const float r = __builtin_amdgcn_rcpf(1.0f + (tiny ? 0.0f : es));
+  const float h = gc * ((z >= 0.0f) ? r : es * r) * (uc + 1.0f);
+  return (tiny && z < 0.0f) ? h * 0x1p-64f : h;
 }
 
 // Sum over the 16 lanes of each DPP row (lanes 16r..16r+15); every lane gets the row's sum.

@@ -438,7 +438,7 @@ def swiglu_oai(g, alpha: float, limit: float) -> np.ndarray:
 def combine(d, pos, w):
     """Router-weighted combine in slot order ([chain]): y[t] = sum_s w[t][s] * d[pos[t][s]],
     float64. Also returns S = sum_s |w[t][s] * d[pos[t][s]]|."""
-    d = np.asarray(d, dtype=np.float64)
+    d = np.asarray(d)    # only the rows pos names are read (the others may hold anything)
     pos = np.asarray(pos)
     w = np.asarray(w, dtype=np.float64)
     T, k = pos.shape
@@ -446,7 +446,7 @@ def combine(d, pos, w):
     S = np.zeros((T, d.shape[1]), dtype=np.float64)
     for t in range(T):
         for s_ in range(k):
-            term = w[t, s_] * d[pos[t, s_]]
+            term = w[t, s_] * np.asarray(d[pos[t, s_]], dtype=np.float64)
             y[t] += term
             S[t] += np.abs(term)
     return y, S

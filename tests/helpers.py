@@ -17,7 +17,10 @@ def torch_mod():
 
 def dev(a):
     torch = torch_mod()
-    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    a = np.ascontiguousarray(a)
+    if not a.flags.writeable:   # torch wants a writable array even to copy it
+        a = a.copy()
+    return torch.from_numpy(a).to("cuda")
 
 
 def bf16_dev(bits):

@@ -153,6 +153,29 @@ def test_route_ties_and_signed_zero():
         assert np.array_equal(host(w), w_ref)
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_swiglu_epilogue_over_the_gate_range(kernel):
+    """Zero activations make g the bias row exactly, so the fused epilogue's h is SwiGLU-OAI of
+    chosen (gate, up) pairs: gates from -200 to 10 (h down to bf16's smallest subnormals and
+    below, where the hardware exp2 underflows), ups across both clamps; within one bf16 ulp."""
+    F = 4096
+    g = np.random.default_rng(5)
+    gate = np.concatenate([np.linspace(-200.0, 10.0, F - 64), g.uniform(-95, -80, 64)])
+    up = g.uniform(-9.0, 9.0, F)
+    bias = np.concatenate([gate, up]).astype(np.float32)[None, :]
+    W = {"q": g.integers(0, 256, (1, 2 * F, 16)).astype(np.uint8),
+         "s": np.full((1, 2 * F, 1), 127, np.uint8), "bias": bias}
+    x = np.zeros((3, 32), dtype=np.uint16)
+    ids = np.zeros((3, 1), dtype=np.int32)
+    log(f"swiglu range {kernel}")
+    mpad, (counts, basep, row_tok, _), (cnt_h, bp_h, _, _) = front(ids, 1, 16)
+    live = live_mask(cnt_h, bp_h, mpad)
+    h = bf16_host(proj(kernel, bf16_dev(x), row_tok, moe.MX4Experts.from_numpy(W), counts, basep,
+                       16, mpad, SWIGLU))
+    ref = oracle.bf16_round(oracle.swiglu_oai(bias.astype(np.float64), ALPHA, LIMIT))
+    assert_bf16_within_ulp(h[live], np.repeat(ref, int(live.sum()), axis=0), f"{kernel} h")
+
+
 @pytest.mark.parametrize("E,k", [(32, 4), (64, 8), (100, 4), (1024, 16)])
 def test_route_nan_rows_give_experts_in_range(E, k):
     """NaN logits rank below every number (a total order): rows with NaNs, all-NaN rows and
