@@ -108,6 +108,33 @@ class Roctx:
 ROCTX = None
 
 
+class Marked:
+    """A timing region, marked in kernel traces: a one-workgroup moe_probe_read of 16 bytes
+    right before and right after it (on the current stream), inside a roctx resume/pause pair.
+    `bench.py --trace-summary` takes the dispatches between such markers."""
+
+    def __init__(self, moe, torch):
+        self.moe = moe
+        self.buf = torch.zeros(4, dtype=torch.int32, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def mark(self):
+        self.moe.moe_probe_read(self.buf, 1, sink=self.sink)
+
+    def __enter__(self):
+        ROCTX.__enter__()
+        self.mark()
+        return self
+
+    def __exit__(self, *exc):
+        self.mark()
+        ROCTX.__exit__(*exc)
+        return False
+
+
+MARK = None
+
+
 class Layer:
     """One MoE layer resident on the GPU with preallocated intermediates (graph-capturable)."""
 
@@ -254,7 +281,7 @@ def kernel_times_us(moe, torch, layers, call, launches, reps, sleep_cycles):
     torch.cuda.synchronize()
     sums = [0.0] * launches
     n = 0
-    with ROCTX:
+    with MARK:
         for _ in range(reps):
             for b0 in range(0, len(layers), per_batch):
                 batch = layers[b0:b0 + per_batch]
@@ -476,11 +503,11 @@ def bench_peaks(moe, torch, sleep_cycles):
         bufs = [torch.ones(nb // 4, dtype=torch.int32, device="cuda") for _ in range(count)]
         sink = torch.zeros(1, dtype=torch.int32, device="cuda")
         best = None
-        for wgs in (cus * 4, cus * 8):
+        for wgs in (cus, cus * 4, cus * 8):
             for b in bufs:
                 moe.moe_probe_read(b, wgs, sink=sink)
             torch.cuda.synchronize()
-            with ROCTX:
+            with MARK:
                 moe.moe_timing_arm(len(bufs))
                 for b in bufs:
                     moe.moe_probe_read(b, wgs, sink=sink)
@@ -496,16 +523,17 @@ def bench_peaks(moe, torch, sleep_cycles):
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
     moe.moe_probe_mfma_bf16(wgs, iters, sink=sink)
     torch.cuda.synchronize()
-    with ROCTX:
+    with MARK:
         moe.moe_timing_arm(4)
         for _ in range(4):
             moe.moe_probe_mfma_bf16(wgs, iters, sink=sink)
         ms = moe.moe_timing_read(4)
         moe.moe_timing_arm(0)
-    fl = wgs * 4 * iters * 8 * 16384.0
+    fl = wgs * 4 * iters * 4 * 32768.0
     out["mfma_bf16_TFLOPs"] = round(fl / (sum(ms) / 4 * 1e-3) / 1e12, 1)
-    out["note"] = ("moe_probe_read: plain grid-stride 16-byte loads; moe_probe_mfma_bf16: "
-                   "v_mfma_f32_16x16x32_bf16 loop, 8 independent chains per wavefront")
+    out["note"] = ("moe_probe_read: grid-stride nontemporal 16-byte loads, best of 1/4/8 "
+                   "workgroups per CU; moe_probe_mfma_bf16: v_mfma_f32_32x32x16_bf16 loop, 4 "
+                   "independent chains per wavefront, 8 workgroups of 4 wavefronts per CU")
     return out
 
 
@@ -677,8 +705,54 @@ def counter_pass(moe, synth, torch, name, with_mx8=False):
     log(f"counter pass {name} done")
 
 
+def trace_summary(path):
+    """Per-kernel duration statistics of a rocprofv3 kernel trace (CSV), over the dispatches
+    inside the marked timing regions (between consecutive one-workgroup probe_read_kernel
+    dispatches) and over all dispatches. Returns {kernel: {...}}."""
+    import csv
+    import statistics
+    rows = list(csv.DictReader(open(path)))
+
+    def grid(r):
+        for key in ("Grid_Size_X", "Grid_Size"):
+            if key in r and r[key]:
+                return int(r[key])
+        return -1
+
+    def wg(r):
+        for key in ("Workgroup_Size_X", "Workgroup_Size"):
+            if key in r and r[key]:
+                return int(r[key])
+        return -2
+
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    inside, marked, allk = False, {}, {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "probe_read_kernel" in name and grid(r) == wg(r):
+            inside = not inside
+            continue
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        allk.setdefault(name, []).append(dur)
+        if inside:
+            marked.setdefault(name, []).append(dur)
+    out = {}
+    for name, ds in marked.items():
+        a = allk[name]
+        out[name] = {"marked_calls": len(ds), "marked_mean_us": statistics.fmean(ds),
+                     "marked_median_us": statistics.median(ds), "marked_min_us": min(ds),
+                     "marked_max_us": max(ds), "all_calls": len(a),
+                     "all_mean_us": statistics.fmean(a)}
+    return out
+
+
 def main():
-    global ROCTX
+    global ROCTX, MARK
+    if len(sys.argv) == 3 and sys.argv[1] == "--trace-summary":
+        for name, st in sorted(trace_summary(sys.argv[2]).items(),
+                               key=lambda kv: -kv[1]["marked_mean_us"] * kv[1]["marked_calls"]):
+            print(json.dumps({"kernel": name, **{k: round(v, 3) for k, v in st.items()}}))
+        return
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); expert parallelism "
@@ -691,6 +765,7 @@ def main():
     moe.lib()   # fail loudly if the HIP library is missing
     torch.cuda.init()
     ROCTX = Roctx()
+    MARK = Marked(moe, torch)
     if args.counter_pass_prefill:
         counter_pass(moe, synth, torch, "prefill_pp512", with_mx8=True)
         return

@@ -393,12 +393,12 @@ int moe_timing_read(float* ms, int n);
  * Attained-peak probes, for measurement only (they are not steps of the chain): the rates a
  * plain kernel reaches on this GPU, reported beside the published peaks.
  *   moe_probe_read: reads every byte of src (device, 16-byte aligned, bytes a multiple of 16)
- *     once with 16-byte loads, 8 in flight per lane, grid-stride over `workgroups` workgroups of
+ *     once with nontemporal 16-byte loads, 8 in flight per lane, grid-stride over `workgroups` workgroups of
  *     256 threads. Algorithmic bytes = bytes. sink (device u32) is written only if the xor of
  *     every word equals 0x9E3779B9 (a guard that keeps the loads; its value means nothing).
  *   moe_probe_mfma_bf16: `workgroups` workgroups of 4 wavefronts, each wavefront issuing
- *     iters x 8 independent v_mfma_f32_16x16x32_bf16 (16*16*32*2 = 16384 flops each), so
- *     flops = workgroups * 4 * iters * 8 * 16384. sink (device f32) is a guard like the read's.
+ *     iters x 4 independent v_mfma_f32_32x32x16_bf16 (32*32*16*2 = 32768 flops each), so
+ *     flops = workgroups * 4 * iters * 4 * 32768. sink (device f32) is a guard like the read's.
  * Errors: MOE_EINVAL for NULL pointers, bytes < 16, workgroups < 1 or iters < 1; MOE_EALIGN for
  *         src or bytes not 16-byte aligned; MOE_ELAUNCH.
  */

@@ -478,7 +478,7 @@ def moe_probe_read(buf, workgroups: int, sink=None, stream=None):
 
 
 def moe_probe_mfma_bf16(workgroups: int, iters: int, sink=None, stream=None):
-    """workgroups * 4 * iters * 8 bf16 MFMAs of 16384 flops each (moe_probe_mfma_bf16)."""
+    """workgroups * 4 * iters * 4 bf16 MFMAs of 32768 flops each (moe_probe_mfma_bf16)."""
     torch = _torch()
     if sink is None:
         sink = torch.zeros(1, dtype=torch.float32, device="cuda")
