@@ -331,23 +331,30 @@ int mx4_moe_decode(const float* logits, const uint16_t* x, int64_t T, int E, int
                    int32_t* ids, float* w, int32_t* counts, int32_t* basep, int32_t* row_tok,
                    int32_t* pos, uint16_t* h, float* d, float* y, void* stream);
 
-#define MOE_DECODE_WS_WORDS 32   /* u32 workspace words of mx4_moe_decode_persistent */
+#define MOE_DECODE_WS_WORDS 544  /* u32 workspace words of mx4_moe_decode_persistent */
 
 /*
  * The same chain as mx4_moe_decode in ONE launch ([chain]'s two stages without the launch
- * boundary between them): a grid of workgroups that can all be resident at once runs the
- * gate_up items (as launch 1) and then the down items (as launch 2); a down item starts
- * streaming its expert rows as soon as it has routed its token and then waits, on a per-token
- * counter, for that token's h rows. Outputs and layouts are those of mx4_moe_decode; routing
- * and the CSR are identical bit for bit, h, d and y within the same tolerances (the gate_up K
- * split is chosen for the grid, so fp32 sums may associate differently; at a given grid the
- * results are deterministic).
+ * boundary between them), built so that every weight byte of the layer is in flight as soon as
+ * the routing is known: a grid of one workgroup per CU (all resident at once) in which every
+ * workgroup routes the tokens itself, then every wavefront issues the loads of a whole work
+ * item (16 weight rows of one pick over half the reduction): gate_up items, and the items of
+ * the workgroup's down tiles (16 output rows of a token, every slot), which wait, holding their
+ * weights in registers, until every workgroup has stored its h rows; d and y are then formed on
+ * chip in slot order. Outputs and layouts are those of mx4_moe_decode; routing and the CSR are
+ * identical bit for bit, h, d and y within the same tolerances (the reduction is split in two
+ * halves here, so fp32 sums may associate differently; at a given grid the results are
+ * deterministic).
  *   ws    u32 [MOE_DECODE_WS_WORDS] device workspace owned by the caller: zero before the first
- *         call; every call leaves words 0..2 and 4.. zero again. Calls that can run
- *         concurrently need distinct workspaces. Word 3 is an error flag the call sets (and
- *         never clears) if a wait ran past its bound (about a second); the outputs of that call
- *         are then invalid. This cannot happen while the grid is resident as sized here.
+ *         call, then left alone (the library keeps its completion counters and a call epoch
+ *         there). Calls that can run concurrently need distinct workspaces. Word 3 is an error
+ *         flag the call sets (and never clears) if a wait ran past its bound (about a second);
+ *         the outputs of that call are then invalid. This cannot happen while the grid is
+ *         resident as sized here.
  *   max_workgroups  0, or a cap on the grid (at least 1) for callers sharing the GPU.
+ * Shapes the one-launch kernel does not take (2k > 8, E > 64, F % 8 != 0, D or F above 3072,
+ * or LDS beyond 64 KB for the grid) run as the two launches of mx4_moe_decode instead; ws is
+ * then untouched.
  * Errors: those of mx4_moe_decode, plus MOE_EINVAL for ws == NULL or max_workgroups < 0,
  *         MOE_EALIGN for ws not 4-byte aligned, MOE_ELAUNCH if the occupancy query fails.
  */

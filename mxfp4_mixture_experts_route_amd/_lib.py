@@ -21,7 +21,7 @@ EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_
            "mx4_moe_gemv", "mx4_moe_gemm", "moe_combine", "mx4_moe_decode", "moe_timing_arm",
            "moe_timing_read", "mx8_quantize", "mx4_moe_gemm_mx8", "moe_router",
            "mx4_moe_decode_persistent", "moe_probe_read", "moe_probe_mfma_bf16")
-MOE_DECODE_WS_WORDS = 32
+MOE_DECODE_WS_WORDS = 544
 MOE_ROUTER_MAX_ROUTED = 16384
 MOE_MX8_GEMM_MAX_K = 4096
 
@@ -393,8 +393,9 @@ def mx4_moe_decode(logits, x, gate_up: MX4Experts, down: MX4Experts, k: int,
 def mx4_moe_decode_persistent(logits, x, gate_up: MX4Experts, down: MX4Experts, k: int, ws,
                               alpha: float = 1.702, limit: float = 7.0, want_d: bool = False,
                               out=None, max_workgroups: int = 0, stream=None):
-    """mx4_moe_decode in one launch. ws: a zeroed int32 device tensor of MOE_DECODE_WS_WORDS
-    words (left zero; word 3 is the error flag). Same outputs as mx4_moe_decode."""
+    """mx4_moe_decode in one launch. ws: an int32 device tensor of MOE_DECODE_WS_WORDS words,
+    zero before its first use and then left to the library (word 3 is the error flag). Same
+    outputs as mx4_moe_decode."""
     torch = _torch()
     _check(logits, torch.float32, "logits")
     _check(x, torch.bfloat16, "x")

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["capi.hip", "pack.hip", "route.hip", "bucket.hip", "gemv.hip", "gemm.hip", "combine.hip",
-           "decode.hip", "timing.hip", "quant.hip",
+           "decode.hip", "decode_layer.hip", "timing.hip", "quant.hip",
            "router.hip", "probe.hip"]
 
 # -packed-fp32-ops: no packed fp32 VALU ops (v_pk_fma_f32 and friends) anywhere in device code.

@@ -37,6 +37,16 @@ __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
   return out;
 }
 
+// The same with the nontemporal hint (weights streamed once: they should not displace what
+// the caches hold for other wavefronts; measured 1.5-2 us faster on the one-launch decode layer)
+__device__ __forceinline__ u32x4_t buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
+  u32x4_t out;
+  __builtin_memcpy(&out, &v, sizeof(out));
+  return out;
+}
+
 __device__ __forceinline__ uint32_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                               uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);

@@ -87,9 +87,8 @@ __device__ __forceinline__ void decode_bookkeeping(const float* __restrict__ log
 
 // Gate_up + SwiGLU-OAI of routed row rho for the units [ubase, ubase + waves / ksplit) of 8 h
 // columns (gate rows j..j+7 and the matching up rows) each, K split over ksplit wavefronts.
-// Routes token rho / k itself. kAtomicH: h is stored with device-scope atomic stores (another
-// XCD's workgroup of the same launch reads it), else plainly.
-template <int SEG, bool kAtomicH>
+// Routes token rho / k itself.
+template <int SEG>
 __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
                                              const uint16_t* __restrict__ x, int E, int k,
                                              const uint8_t* __restrict__ q,
@@ -114,8 +113,9 @@ __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
   lds_dma_copy(x + (size_t)t * K, row_bytes, xs, wave, nthreads >> 6);
   __builtin_amdgcn_sched_barrier(0);
   const size_t zoff = ((size_t)row_bytes + 1023) & ~(size_t)1023;
-  uint8_t* const slot0 = xs + zoff + 64;   // wavefront 0's 1 KB: logits, then the pick at +512
-  int* const pick = reinterpret_cast<int*>(slot0 + 512);
+  // wavefront 0's 1 KB: the logits row, the rank keys at +256, the pick at +768
+  uint8_t* const slot0 = xs + zoff + 64;
+  int* const pick = reinterpret_cast<int*>(slot0 + 768);
   if (wave == 0) {
     int e0;
     if (E <= kWave) {   // one logit per lane: rank against the row in LDS
@@ -124,7 +124,8 @@ __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rl, (__attribute__((address_space(3))) void*)lrow, 4, (uint32_t)lane * 4, 0, 0, 0);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      e0 = rank_pick(wave_rank_lds(lrow, E), slot);   // lrow: 0 past E (read past the resource)
+      // lrow: 0 past E (read past the resource)
+      e0 = rank_pick(wave_rank_lds(lrow, reinterpret_cast<uint64_t*>(slot0 + 256), E), slot);
     } else {
       float lv[kRoutePerLane];
       wave_topk_load(logits + (size_t)t * E, E, lv);
@@ -198,16 +199,9 @@ __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
 #pragma unroll
       for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_bits(swiglu_oai(acc[i], up[i], alpha, limit));
       uint16_t* dst = h + (size_t)rho * F + j0;
-      if (kAtomicH && j0 + 4 <= F) {   // 8-byte aligned: F and j0 are multiples of 4
-        uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
-        __hip_atomic_store(d32, hb[0] | (hb[1] << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(d32 + 1, hb[2] | (hb[3] << 16), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (j0 + i < F) dst[i] = (uint16_t)hb[i];
-      }
+      for (int i = 0; i < 4; ++i)
+        if (j0 + i < F) dst[i] = (uint16_t)hb[i];
     }
   }
 }
@@ -228,7 +222,7 @@ decode_gate_up_kernel(const float* __restrict__ logits, const uint16_t* __restri
     return;
   }
   const int upw = ((int)blockDim.x >> 6) / ksplit;
-  gate_up_item<SEG, false>(logits, x, E, k, q, s, bias, N, K, alpha, limit, ksplit,
+  gate_up_item<SEG>(logits, x, E, k, q, s, bias, N, K, alpha, limit, ksplit,
                            (int)blockIdx.y, (int)blockIdx.x * upw, h, xs);
 }
 
@@ -313,212 +307,13 @@ decode_down_kernel(const uint16_t* __restrict__ h, int E, int k, const int32_t* 
   }
 }
 
-// ---------------------------------------------------------------------------------------------
-// One-launch layer (mx4_moe_decode_persistent). The same items as the two launches above, run
-// by one grid: workgroup g takes gate_up items g, g + G, ... and then down items g, g + G, ....
-// A down item issues its weight loads as soon as it has routed its token, and only then waits
-// until every gate_up item of that token has published its h rows (a per-token counter), so the
-// down weights stream while the gate_up work is still in flight and no launch boundary sits
-// between the two stages. The host caps G at the number of workgroups that can be resident at
-// once, so every item a workgroup waits for belongs to a workgroup that is running (or will run
-// as soon as another kernel's workgroups leave); the wait is bounded all the same, and flags
-// an error in the workspace instead of spinning on.
-// ---------------------------------------------------------------------------------------------
-
-constexpr int kWsDone = 4;                 // workspace: [0..3] reserved/counters, [4..4+T) done
-constexpr int kWsExited = 2, kWsError = 3;
-constexpr uint32_t kSpinMax = 1u << 20;    // polls of about a microsecond each
-
-template <int SEG>
-__device__ __forceinline__ void down_item_persistent(
-    const float* __restrict__ logits, int E, int k, const uint8_t* __restrict__ q,
-    const uint8_t* __restrict__ s, const float* __restrict__ bias, int D, int F, int ksplit,
-    int t, int unit, const uint16_t* __restrict__ h, uint32_t* __restrict__ ws, uint32_t need,
-    float* __restrict__ d, float* __restrict__ y, uint8_t* xs) {
-  const int KB = F >> 5;
-  const int C = (KB + kChunkBlocks - 1) / kChunkBlocks;
-  const int tid = (int)threadIdx.x;
-  const int nthreads = (int)blockDim.x;
-  const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, lg = lane >> 4;
-  const uint32_t row_bytes = (uint32_t)F * 2;
-  const bool active = wave < k * ksplit;   // wavefronts past k slots x ksplit parts only wait
-  const int slot = active ? wave / ksplit : 0, part = wave % ksplit;
-
-  // 1. route token t (each wavefront: the expert of its slot; wavefront 0 also the weights)
-  int e;
-  float wsl = 0.0f;   // wavefront 0, lane sl: routing weight of slot sl
-  if (E <= kWave) {
-    const float v = lane < E ? logits[(size_t)t * E + lane] : 0.0f;
-    const int rank = wave_rank_row(logits + (size_t)t * E, E);
-    e = rank_pick(rank, slot);
-    if (wave == 0) {
-      int my_id = 0;
-      float my_v = 0.0f;
-      for (int r = 0; r < k; ++r) {
-        const int id = rank_pick(rank, r);
-        const float vr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), id));
-        if (lane == r) {
-          my_id = id;
-          my_v = vr;
-        }
-      }
-      (void)my_id;
-      wsl = topk_weight(my_v, k);
-    }
-  } else {
-    float lv[kRoutePerLane];
-    wave_topk_load(logits + (size_t)t * E, E, lv);
-    int my_id;
-    float my_v;
-    wave_topk_select(lv, E, k, my_id, my_v);
-    e = __shfl(my_id, slot);
-    if (wave == 0) wsl = topk_weight(my_v, k);
-  }
-
-  e = min(max(e, 0), E - 1);   // in [0, E) by the total order; clamped as in gate_up_item
-
-  // 2. this wavefront's down rows in flight before the wait
-  int cb, ce, Cp;
-  k_part_range(C, part, ksplit, cb, ce, Cp);
-  const int n = unit * 16 + lr;
-  Mx4Wave<SEG> wv;
-  wv.init(q, s, e, n, active && n < D, D, F, ce);
-  float b4[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int nn = unit * 16 + 4 * lg + i;
-    b4[i] = (active && nn < D && bias && part == 0) ? bias[(size_t)e * D + nn] : 0.0f;
-  }
-  if (active) wv.load_segment(cb);
-
-  // 3. wait until every gate_up item of token t has published its h rows (bounded)
-  if (tid == 0) {
-    uint32_t it = 0;
-    while (__hip_atomic_load(ws + kWsDone + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++it == kSpinMax) {
-        __hip_atomic_store(ws + kWsError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-  }
-  __syncthreads();
-
-  // 4. the token's k rows of h (routed-row order: slot s is row t*k + s) into LDS, read with
-  // device-scope atomic loads (written by other workgroups of this launch)
-  const uint32_t* h32 = reinterpret_cast<const uint32_t*>(h + (size_t)t * k * F);
-  uint32_t* x32 = reinterpret_cast<uint32_t*>(xs);
-  const int ndw = k * F / 2;
-  for (int i = tid; i < ndw; i += nthreads)
-    x32[i] = __hip_atomic_load(h32 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const size_t zero_off = ((size_t)k * row_bytes + 1023) & ~(size_t)1023;
-  if (tid < 4) *reinterpret_cast<uint4*>(xs + zero_off + tid * 16) = make_uint4(0u, 0u, 0u, 0u);
-  const uint8_t* xzero = xs + zero_off;
-  f32x4_t* red = reinterpret_cast<f32x4_t*>(xs + zero_off + 64);
-  __syncthreads();
-
-  // 5. the products; every wavefront's partial rows meet in LDS; wavefront 0 forms d of each
-  // slot (parts in order, bias in part 0) and y = sum over slots, in slot order, of w * d
-  f32x4_t acc = {b4[0], b4[1], b4[2], b4[3]};
-  f32x4_t acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (active) {
-    for (int c0 = cb; c0 < ce; c0 += SEG) {
-      if (c0 > cb) wv.load_segment(c0);
-      wv.run_segment(c0, KB, xs + (size_t)slot * row_bytes, xzero, lr == 0, acc, acc1);
-    }
-    acc += acc1;
-    red[wave * 64 + lane] = acc;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    float yv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int sl = 0; sl < k; ++sl) {
-      f32x4_t ds = red[(sl * ksplit) * 64 + lane];
-      for (int pp = 1; pp < ksplit; ++pp) ds += red[(sl * ksplit + pp) * 64 + lane];
-      const float ws_w = __shfl(wsl, sl);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) yv[i] = fmaf(ws_w, ds[i], yv[i]);
-      if (d && lr == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int nn = unit * 16 + 4 * lg + i;
-          if (nn < D) d[((size_t)t * k + sl) * D + nn] = ds[i];
-        }
-      }
-    }
-    if (lr == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int nn = unit * 16 + 4 * lg + i;
-        if (nn < D) y[(size_t)t * D + nn] = yv[i];
-      }
-    }
-  }
-  __syncthreads();   // the LDS is free for the next item
-}
-
-template <int SEG>
-__global__ void __launch_bounds__(kDecMaxThreads)
-decode_layer_kernel(const float* __restrict__ logits, const uint16_t* __restrict__ x, int T,
-                    int E, int k, const uint8_t* __restrict__ gq, const uint8_t* __restrict__ gs,
-                    const float* __restrict__ gb, int N, int D, const uint8_t* __restrict__ dq,
-                    const uint8_t* __restrict__ dsc, const float* __restrict__ db, float alpha,
-                    float limit, int ks1, int ks2, int groups, int n_down,
-                    int32_t* __restrict__ ids, float* __restrict__ w,
-                    int32_t* __restrict__ counts, int32_t* __restrict__ basep,
-                    int32_t* __restrict__ row_tok, int32_t* __restrict__ pos,
-                    uint16_t* __restrict__ h, float* __restrict__ d, float* __restrict__ y,
-                    uint32_t* __restrict__ ws) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
-  const int G = (int)gridDim.x, g = (int)blockIdx.x, tid = (int)threadIdx.x;
-  const int R = T * k, F = N >> 1;
-  const int n_up = R * groups;
-  const int upw = ((int)blockDim.x >> 6) / ks1;
-  const int n_items = n_up + n_down;
-  // one list of items, gate_up first: workgroup g takes items g, g + G, ...; so every
-  // workgroup finishes its gate_up items before it waits in a down item, and workgroups with
-  // no gate_up item start their down items (and their weight streams) at once
-  // the routing and CSR for the caller, by the last workgroup: first if it has no gate_up item
-  // (off the critical path), else after its items
-  const bool book = g == G - 1;
-  if (book && g >= n_up) {
-    decode_bookkeeping(logits, T, E, k, ids, w, counts, basep, row_tok, pos);
-  }
-  const uint32_t need = (uint32_t)(k * groups);   // gate_up items of one token
-  int i = g;
-  for (; i < n_up; i += G) {   // the gate_up items of this workgroup, then its down items
-    const int rho = i % R, grp = i / R;
-    __syncthreads();   // the LDS is free
-    gate_up_item<SEG, true>(logits, x, E, k, gq, gs, gb, N, D, alpha, limit, ks1, rho,
-                            grp * upw, h, xs);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // this wavefront's h stores are acknowledged
-    __syncthreads();
-    if (tid == 0)
-      __hip_atomic_fetch_add(ws + kWsDone + rho / k, 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-  }
-  for (; i < n_items; i += G) {
-    const int j = i - n_up;
-    __syncthreads();
-    down_item_persistent<SEG>(logits, E, k, dq, dsc, db, D, F, ks2, j % T, j / T, h, ws, need,
-                              d, y, xs);
-  }
-  if (book && g < n_up) {
-    __syncthreads();
-    decode_bookkeeping(logits, T, E, k, ids, w, counts, basep, row_tok, pos);
-  }
-  // the last workgroup to leave resets the counters for the next call
-  __syncthreads();
-  if (tid == 0 &&
-      __hip_atomic_fetch_add(ws + kWsExited, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-          (uint32_t)G - 1) {
-    for (int tt = 0; tt < T; ++tt)
-      __hip_atomic_store(ws + kWsDone + tt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(ws + kWsExited, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
 }  // namespace moe
+
+int moe_launch_decode_two(const float* logits, const uint16_t* x, int64_t T, int E, int k,
+                          const mx4_experts* w_gu, const mx4_experts* w_dn, float alpha,
+                          float limit, int32_t* ids, float* w, int32_t* counts, int32_t* basep,
+                          int32_t* row_tok, int32_t* pos, uint16_t* h, float* d, float* y,
+                          hipStream_t stream);
 
 extern "C" int mx4_moe_decode(const float* logits, const uint16_t* x, int64_t T, int E, int k,
                               const mx4_experts* w_gu, const mx4_experts* w_dn, float alpha,
@@ -539,6 +334,18 @@ extern "C" int mx4_moe_decode(const float* logits, const uint16_t* x, int64_t T,
       misaligned(w_gu->s) || misaligned(w_dn->s) || (((uintptr_t)logits) & 3) ||
       (((uintptr_t)y) & 3) || (d && (((uintptr_t)d) & 3)))
     return MOE_EALIGN;
+  return moe_launch_decode_two(logits, x, T, E, k, w_gu, w_dn, alpha, limit, ids, w, counts,
+                               basep, row_tok, pos, h, d, y, (hipStream_t)stream);
+}
+
+// The two launches of mx4_moe_decode (arguments already checked); also what
+// mx4_moe_decode_persistent runs for shapes its one-launch kernel does not take.
+int moe_launch_decode_two(const float* logits, const uint16_t* x, int64_t T, int E, int k,
+                          const mx4_experts* w_gu, const mx4_experts* w_dn, float alpha,
+                          float limit, int32_t* ids, float* w, int32_t* counts, int32_t* basep,
+                          int32_t* row_tok, int32_t* pos, uint16_t* h, float* d, float* y,
+                          hipStream_t st) {
+  const int D = w_gu->K, N = w_gu->N, F = N / 2;
   const int C1 = (D / 32 + moe::kChunkBlocks - 1) / moe::kChunkBlocks;
   const int C2 = (F / 32 + moe::kChunkBlocks - 1) / moe::kChunkBlocks;
   const int R = (int)T * k;
@@ -564,7 +371,6 @@ extern "C" int mx4_moe_decode(const float* logits, const uint16_t* x, int64_t T,
       (int64_t)D * (F / 32) * 16 >= ((int64_t)1 << 31))
     return MOE_ESHAPE;
 
-  hipStream_t st = (hipStream_t)stream;
   const dim3 g1((unsigned)((units1 + upw1 - 1) / upw1), (unsigned)(R + 1));
   moe::launch(moe::decode_gate_up_kernel<moe::kGvSeg>, g1, dim3(64 * waves1), lds1, st, logits, x,
               (int)T, E, k, w_gu->q, w_gu->s, w_gu->bias, N, D, alpha, limit, ks1, ids, w, counts,
@@ -573,70 +379,5 @@ extern "C" int mx4_moe_decode(const float* logits, const uint16_t* x, int64_t T,
   const dim3 g2((unsigned)((D + 15) / 16), (unsigned)T);
   moe::launch(moe::decode_down_kernel<moe::kGvSeg>, g2, dim3(64 * waves2), lds2, st, h, E, k, ids, w,
               w_dn->q, w_dn->s, w_dn->bias, D, F, ks2, d, y);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
-}
-
-extern "C" int mx4_moe_decode_persistent(const float* logits, const uint16_t* x, int64_t T, int E,
-                                         int k, const mx4_experts* w_gu, const mx4_experts* w_dn,
-                                         float alpha, float limit, int32_t* ids, float* w,
-                                         int32_t* counts, int32_t* basep, int32_t* row_tok,
-                                         int32_t* pos, uint16_t* h, float* d, float* y,
-                                         uint32_t* ws, int max_workgroups, void* stream) {
-  if (!logits || !x || !w_gu || !w_dn || !ids || !w || !counts || !basep || !row_tok || !pos ||
-      !h || !y || !ws || !w_gu->q || !w_gu->s || !w_dn->q || !w_dn->s || T < 1 || E < 1 ||
-      k < 1 || k > E || k > MOE_MAX_K || max_workgroups < 0)
-    return MOE_EINVAL;
-  if (T > MOE_DECODE_MAX_T || E > MOE_MAX_E || k > MOE_DECODE_MAX_K) return MOE_ESHAPE;
-  const int D = w_gu->K, N = w_gu->N, F = N / 2;
-  if (w_gu->E != E || w_dn->E != E || N < 2 || (N & 1) || D < 32 || (D & 31) || w_dn->N != D ||
-      w_dn->K != F || (F & 31))
-    return MOE_ESHAPE;
-  auto misaligned = [](const void* p) { return (((uintptr_t)p) & 15) != 0; };
-  if (misaligned(x) || misaligned(h) || misaligned(w_gu->q) || misaligned(w_dn->q) ||
-      misaligned(w_gu->s) || misaligned(w_dn->s) || (((uintptr_t)logits) & 3) ||
-      (((uintptr_t)y) & 3) || (d && (((uintptr_t)d) & 3)) || (((uintptr_t)ws) & 3))
-    return MOE_EALIGN;
-  if ((int64_t)N * (D / 32) * 16 >= ((int64_t)1 << 31) ||
-      (int64_t)D * (F / 32) * 16 >= ((int64_t)1 << 31))
-    return MOE_ESHAPE;
-  const int C1 = (D / 32 + moe::kChunkBlocks - 1) / moe::kChunkBlocks;
-  const int C2 = (F / 32 + moe::kChunkBlocks - 1) / moe::kChunkBlocks;
-  const int R = (int)T * k;
-  constexpr int kWaves = moe::kDecMaxThreads / 64;   // 8 wavefronts per workgroup
-  int ks2 = moe::gv_ksplit(C2);
-  while (ks2 > 1 && k * ks2 > kWaves) --ks2;
-  const int units1 = (F + 7) / 8;
-  const int n_down = (int)T * ((D + 15) / 16);
-  const size_t lds_a = (((size_t)D * 2 + 1023) & ~(size_t)1023) + 64 + (size_t)kWaves * 64 * 16;
-  const size_t lds_b = (((size_t)k * F * 2 + 1023) & ~(size_t)1023) + 64 + (size_t)kWaves * 64 * 16;
-  const size_t lds = lds_a > lds_b ? lds_a : lds_b;
-  if (lds > 65536) return MOE_ESHAPE;
-
-  // the grid: every item is reachable by workgroups that can all be resident at once
-  auto kernel = moe::decode_layer_kernel<moe::kGvSeg>;
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel),
-                                                   moe::kDecMaxThreads, lds) != hipSuccess ||
-      per_cu < 1)
-    return MOE_ELAUNCH;
-  int64_t cap = (int64_t)per_cu * cus;
-  if (max_workgroups > 0 && cap > max_workgroups) cap = max_workgroups;
-  // the gate_up K split: the engine's own choice (2 at gpt-oss K) when its items fit in one
-  // round of the grid, else none (a wavefront then runs its K in segments), which halves the
-  // items; whole units per workgroup either way
-  int ks1 = moe::gv_ksplit(C1);
-  if (kWaves % ks1 != 0) ks1 = 2;
-  if ((int64_t)R * ((units1 + kWaves / ks1 - 1) / (kWaves / ks1)) > cap) ks1 = 1;
-  const int upw1 = kWaves / ks1;
-  const int groups = (units1 + upw1 - 1) / upw1;
-  const int n_up = R * groups;
-  int64_t G = (int64_t)n_up + n_down;
-  if (G > cap) G = cap;
-  moe::launch(kernel, dim3((unsigned)G), dim3(moe::kDecMaxThreads), lds, (hipStream_t)stream,
-              logits, x, (int)T, E, k, w_gu->q, w_gu->s, w_gu->bias, N, D, w_dn->q, w_dn->s,
-              w_dn->bias, alpha, limit, ks1, ks2, groups, n_down, ids, w, counts, basep, row_tok,
-              pos, h, d, y, ws);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

@@ -121,7 +121,7 @@ struct Mx4Wave {
 #pragma unroll
     for (int i = 0; i < SEG / 4; ++i) {
       const int gi = (c0 + 4 * i) / 4;   // c0 is a multiple of 4: whole groups
-      const u32x4_t v = buf_load16(rs, gi < G ? so : kOOB, (uint32_t)gi * N * 16);
+      const u32x4_t v = buf_load16_nt(rs, gi < G ? so : kOOB, (uint32_t)gi * N * 16);
       sc[4 * i + 0] = v[0];
       sc[4 * i + 1] = v[1];
       sc[4 * i + 2] = v[2];
@@ -130,7 +130,7 @@ struct Mx4Wave {
       for (int k = 0; k < 4; ++k) {
         const int c = c0 + 4 * i + k;
         const uint32_t off = (c >= ce) ? kOOB : (c < C - 1 ? wo : wol);
-        wq[4 * i + k] = buf_load16(rq, off, (uint32_t)c * N * (kChunkBlocks * 16));
+        wq[4 * i + k] = buf_load16_nt(rq, off, (uint32_t)c * N * (kChunkBlocks * 16));
       }
       __builtin_amdgcn_sched_barrier(0);
     }

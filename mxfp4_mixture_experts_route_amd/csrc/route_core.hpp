@@ -14,14 +14,35 @@ namespace moe {
 
 constexpr int kRoutePerLane = MOE_MAX_E / kWave;     // logits held per lane
 
-// a ranks before b in a total order of (value, id): a number before a NaN (a NaN logit ranks
+// The top-k order is a total order of (value, id): a number before a NaN (a NaN logit ranks
 // below every number, -inf included), the larger number first, equal values (-0.0 == +0.0) and
 // two NaNs by the lower id. Being total, it gives every logit of a row a distinct rank, so the
 // first k ranks always name k distinct experts in [0, E), whatever the row holds.
+//
+// It is computed through an integer key: a ranks before b exactly when key(a) > key(b). The high
+// word maps the float monotonically onto unsigned integers (sign bit set: all bits inverted;
+// clear: the sign bit set), -0 onto +0's word and every NaN onto 0, below -inf's 0x007FFFFF;
+// the low word is ~id, so that the lower id is the larger key. Key 0 is below every key of a
+// real (value, id) (whose low word is at least ~0x7FFFFFFF) and serves as "none". One 64-bit
+// compare per pair keeps the rank loops on the vector ALU (boolean combinations of float
+// compares become lane-mask logic on the scalar unit, a round trip per element).
+__device__ __forceinline__ uint64_t rank_key(float v, int id) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t mag = b & 0x7FFFFFFFu;
+  uint32_t hi = (b >> 31) ? ~b : (b | 0x80000000u);
+  hi = mag == 0u ? 0x80000000u : hi;          // -0 as +0
+  hi = mag > 0x7F800000u ? 0u : hi;           // NaN below every number
+  return ((uint64_t)hi << 32) | (uint64_t)(~(uint32_t)id);
+}
+
 __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-  const bool na = va != va, nb = vb != vb;
-  const bool lower_id = ia < ib;
-  return (nb & (!na | lower_id)) | (!na & !nb & ((va > vb) | ((va == vb) & lower_id)));
+  return rank_key(va, ia) > rank_key(vb, ib);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Logits of one row for wave_topk_select: lane l holds experts j*64 + l (0 past E).
@@ -37,74 +58,71 @@ __device__ __forceinline__ void wave_topk_load(const float* __restrict__ row, in
 
 // The k best experts of one logits row (E <= MOE_MAX_E, k <= min(E, MOE_MAX_K)) held as by
 // wave_topk_load. Lane r < k ends with the r-th pick in (my_id, my_v); other lanes' outputs are
-// unspecified. k rounds of a wavefront arg-best over per-lane candidates; no LDS.
+// unspecified. k rounds of a wavefront arg-max over the lanes' best remaining keys; no LDS.
 __device__ __forceinline__ void wave_topk_select(const float (&v)[kRoutePerLane], int E, int k,
                                                  int& my_id, float& my_v) {
   const int lane = (int)(threadIdx.x & 63);
-  uint32_t taken = 0;                 // bit j: expert j*64+lane already chosen (or absent)
+  uint64_t key[kRoutePerLane];   // 0: absent or already chosen
 #pragma unroll
-  for (int j = 0; j < kRoutePerLane; ++j)
-    if (j * kWave + lane >= E) taken |= 1u << j;
-
+  for (int j = 0; j < kRoutePerLane; ++j) {
+    const int e = j * kWave + lane;
+    key[j] = e < E ? rank_key(v[j], e) : 0u;
+  }
   my_id = 0;
   my_v = 0.0f;
   for (int r = 0; r < k; ++r) {
-    // this lane's best remaining candidate
-    float bv = 0.0f;
-    int bi = 0x7FFFFFFF;
+    uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < kRoutePerLane; ++j) {
-      const int e = j * kWave + lane;
-      if (!(taken & (1u << j)) && (bi == 0x7FFFFFFF || ranks_before(v[j], e, bv, bi))) {
-        bv = v[j];
-        bi = e;
-      }
-    }
-    // wavefront arg-best (lanes without a candidate carry id INT_MAX and never win)
+    for (int j = 0; j < kRoutePerLane; ++j) best = key[j] > best ? key[j] : best;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m);
-      const int oi = __shfl_xor(bi, m);
-      if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ranks_before(ov, oi, bv, bi))) {
-        bv = ov;
-        bi = oi;
+      const uint64_t o = shfl_xor_u64(best, m);
+      best = o > best ? o : best;
+    }
+    const int id = (int)~(uint32_t)best;   // k <= E: a real key won
+    const int jw = id >> 6, lw = id & 63;
+    float cand = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kRoutePerLane; ++j) {
+      if (j == jw) {
+        cand = v[j];
+        if (lane == lw) key[j] = 0u;
       }
     }
+    const float vw = __shfl(cand, lw);
     if (lane == r) {
-      my_id = bi;
-      my_v = bv;
+      my_id = id;
+      my_v = vw;
     }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
   }
 }
 
 // E <= 64: the rank of every lane's logit among the row's E logits (the number that rank before
 // it), the lane of rank r holding pick r; E or more for lanes >= E. From the logits row staged in
-// LDS (row[0..63]; what lies past E is never compared): eight values per step come as broadcast
-// LDS reads and every compare is independent of the previous one, so the steps overlap. (A
-// broadcast of each lane's value by v_readlane waits for the scalar register every step:
-// ~115 cycles a step, 1.5 us for E = 32.)
-__device__ __forceinline__ int wave_rank_lds(const float* row, int E) {
+// LDS (row[0..63]; what lies past E is never compared) and 64 keys of LDS scratch of the calling
+// wavefront: every lane writes its key, then reads all of them eight at a time (broadcast reads;
+// the LDS operations of a wavefront complete in order) and counts the larger ones.
+__device__ __forceinline__ int wave_rank_lds(const float* row, uint64_t* keys, int E) {
   const int lane = (int)(threadIdx.x & 63);
-  const float v = row[lane];
+  const uint64_t mk = rank_key(row[lane], lane);
+  keys[lane] = lane < E ? mk : 0u;
   int rank = 0;
-  for (int j0 = 0; j0 < E; j0 += 8) {
-    const float4 a = *reinterpret_cast<const float4*>(row + j0);
-    const float4 b = *reinterpret_cast<const float4*>(row + j0 + 4);
-    const float vj[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      rank += (j0 + u < E && ranks_before(vj[u], j0 + u, v, lane)) ? 1 : 0;
+  for (int j0 = 0; j0 < E; j0 += 8) {   // j0 + 8 <= 64; keys past E are 0 and never count
+    const ulonglong2 a0 = *reinterpret_cast<const ulonglong2*>(keys + j0);
+    const ulonglong2 a1 = *reinterpret_cast<const ulonglong2*>(keys + j0 + 2);
+    const ulonglong2 a2 = *reinterpret_cast<const ulonglong2*>(keys + j0 + 4);
+    const ulonglong2 a3 = *reinterpret_cast<const ulonglong2*>(keys + j0 + 6);
+    rank += (a0.x > mk) + (a0.y > mk) + (a1.x > mk) + (a1.y > mk) + (a2.x > mk) +
+            (a2.y > mk) + (a3.x > mk) + (a3.y > mk);
   }
   return lane < E ? rank : E + lane;
 }
 
-// The same ranks from a logits row in memory (global or LDS; E <= 64): eight values per step
-// by loads every lane makes at the same address, then the tail one at a time, so nothing past
-// E is read and the compares are independent of each other (no cross-lane step in the chain).
+// The same ranks from a logits row in memory (E <= 64): eight values per step by loads every
+// lane makes at the same address, then the tail one at a time, so nothing past E is read.
 __device__ __forceinline__ int wave_rank_row(const float* __restrict__ row, int E) {
   const int lane = (int)(threadIdx.x & 63);
-  const float v = lane < E ? row[lane] : 0.0f;
+  const uint64_t mk = rank_key(lane < E ? row[lane] : 0.0f, lane);
   int rank = 0;
   int j0 = 0;
   for (; j0 + 8 <= E; j0 += 8) {
@@ -112,9 +130,9 @@ __device__ __forceinline__ int wave_rank_row(const float* __restrict__ row, int 
 #pragma unroll
     for (int u = 0; u < 8; ++u) vj[u] = row[j0 + u];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) rank += ranks_before(vj[u], j0 + u, v, lane) ? 1 : 0;
+    for (int u = 0; u < 8; ++u) rank += rank_key(vj[u], j0 + u) > mk;
   }
-  for (; j0 < E; ++j0) rank += ranks_before(row[j0], j0, v, lane) ? 1 : 0;
+  for (; j0 < E; ++j0) rank += rank_key(row[j0], j0) > mk;
   return lane < E ? rank : E + lane;
 }
 
