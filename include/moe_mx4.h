@@ -22,6 +22,7 @@
  *   mx4_moe_decode  logits + x -> routing, CSR, h, (d), y
  *   mx4_moe_decode_persistent  the same in one launch (a resident grid; down weights stream
  *                   while gate_up is still running)
+ *   mx4_moe_decode_persistent_static  the same with a library-held workspace (no allocation)
  *
  * Sources (web pages on the daScript repository's dasLLAMA engine; cited by tag below):
  *   [fusion]  PR #3579 "dasLLAMA gpt-oss arc", commit log, the Metal fusion-lane commit: the
@@ -364,6 +365,31 @@ int mx4_moe_decode_persistent(const float* logits, const uint16_t* x, int64_t T,
                               int32_t* basep, int32_t* row_tok, int32_t* pos, uint16_t* h,
                               float* d, float* y, uint32_t* ws, int max_workgroups,
                               void* stream);
+
+/*
+ * mx4_moe_decode_persistent for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no workspace argument.
+ * The workspace is the library's own, a file-scope device array of MOE_DECODE_WS_WORDS u32 words
+ * (2176 bytes) that every GPU the library runs on holds until the process ends. Nothing is
+ * allocated: a call that runs the one-launch kernel first enqueues a one-workgroup kernel that
+ * zeroes that array (a kernel, not a memset, so the call can be captured), then the layer kernel;
+ * the shapes the one-launch kernel does not take run as the two launches of mx4_moe_decode,
+ * which use no workspace. The array has the same size at every shape (it holds counters, not
+ * data); shapes beyond the limits of mx4_moe_decode_persistent are rejected with its errors.
+ * Every call on a GPU shares that GPU's array: calls that can overlap on one GPU (other streams,
+ * other threads) race, and only one may be in flight per GPU at a time. The workspace's error
+ * flag (a wait past its bound) is not reported by this variant.
+ * Arguments and outputs are those of mx4_moe_decode_persistent without ws; for equal arguments
+ * the outputs are bit-identical to it.
+ * Errors: those of mx4_moe_decode_persistent other than the ws ones, plus MOE_ELAUNCH if the
+ *         array's device address cannot be obtained.
+ */
+int mx4_moe_decode_persistent_static(const float* logits, const uint16_t* x, int64_t T, int E,
+                                     int k, const mx4_experts* w_gu, const mx4_experts* w_dn,
+                                     float alpha, float limit, int32_t* ids, float* w,
+                                     int32_t* counts, int32_t* basep, int32_t* row_tok,
+                                     int32_t* pos, uint16_t* h, float* d, float* y,
+                                     int max_workgroups, void* stream);
 
 /*
  * Router-weighted combine ([chain]: routing-weighted sum of the expert rows in slot order).

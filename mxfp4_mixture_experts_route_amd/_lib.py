@@ -20,7 +20,8 @@ MOE_MAX_K, MOE_MAX_E, MOE_MAX_TILE_M = 16, 1024, 256
 EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_pack_experts",
            "mx4_moe_gemv", "mx4_moe_gemm", "moe_combine", "mx4_moe_decode", "moe_timing_arm",
            "moe_timing_read", "mx8_quantize", "mx4_moe_gemm_mx8", "moe_router",
-           "mx4_moe_decode_persistent", "moe_probe_read", "moe_probe_mfma_bf16")
+           "mx4_moe_decode_persistent", "mx4_moe_decode_persistent_static", "moe_probe_read",
+           "moe_probe_mfma_bf16")
 MOE_DECODE_WS_WORDS = 544
 MOE_ROUTER_MAX_ROUTED = 16384
 MOE_MX8_GEMM_MAX_K = 4096
@@ -82,6 +83,9 @@ def lib() -> ctypes.CDLL:
         L.mx4_moe_decode_persistent.restype = ci
         L.mx4_moe_decode_persistent.argtypes = [vp, vp, i64, ci, ci, pe, pe, cf, cf, vp, vp, vp,
                                                 vp, vp, vp, vp, vp, vp, vp, ci, vp]
+        L.mx4_moe_decode_persistent_static.restype = ci
+        L.mx4_moe_decode_persistent_static.argtypes = [vp, vp, i64, ci, ci, pe, pe, cf, cf, vp,
+                                                       vp, vp, vp, vp, vp, vp, vp, vp, ci, vp]
         L.moe_router.restype = ci
         L.moe_router.argtypes = [vp, vp, vp, i64, ci, ci, ci, ci, i64, vp, vp, vp, vp, vp, vp,
                                  vp, vp, vp]
@@ -417,6 +421,23 @@ def mx4_moe_decode_persistent(logits, x, gate_up: MX4Experts, down: MX4Experts, 
           _ptr(o["counts"]), _ptr(o["basep"]), _ptr(o["row_tok"]), _ptr(o["pos"]), _ptr(o["h"]),
           _ptr(o.get("d")), _ptr(o["y"]), _ptr(ws), int(max_workgroups), _stream(stream))
     return o
+
+
+def mx4_moe_decode_persistent_static(logits, x, gate_up: MX4Experts, down: MX4Experts, k: int,
+                                     out: dict, alpha: float = 1.702, limit: float = 7.0,
+                                     max_workgroups: int = 0, stream=None):
+    """mx4_moe_decode_persistent with the library's own workspace (allocates nothing). out: the
+    caller's output tensors, keys ids, w, counts, basep, row_tok, pos, h, y and optionally d."""
+    torch = _torch()
+    _check(logits, torch.float32, "logits")
+    _check(x, torch.bfloat16, "x")
+    T, E = logits.shape
+    _call("mx4_moe_decode_persistent_static", _ptr(logits), _ptr(x), T, E, k,
+          ctypes.byref(gate_up.c), ctypes.byref(down.c), float(alpha), float(limit),
+          _ptr(out["ids"]), _ptr(out["w"]), _ptr(out["counts"]), _ptr(out["basep"]),
+          _ptr(out["row_tok"]), _ptr(out["pos"]), _ptr(out["h"]), _ptr(out.get("d")),
+          _ptr(out["y"]), int(max_workgroups), _stream(stream))
+    return out
 
 
 def moe_timing_arm(n: int) -> None:

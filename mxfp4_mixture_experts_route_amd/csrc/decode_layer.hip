@@ -31,6 +31,8 @@
 //  * No workgroup waits for anything but that count, which every workgroup reaches before it
 //    waits, and the host sizes the grid to what can be resident at once; the wait is bounded all
 //    the same (an error flag in the workspace instead of a hang).
+#include <mutex>
+
 #include "gemv_core.hpp"
 #include "launch.hpp"
 #include "route_core.hpp"
@@ -606,14 +608,48 @@ int moe_launch_decode_two(const float* logits, const uint16_t* x, int64_t T, int
                           int32_t* row_tok, int32_t* pos, uint16_t* h, float* d, float* y,
                           hipStream_t stream);
 
-extern "C" int mx4_moe_decode_persistent(const float* logits, const uint16_t* x, int64_t T, int E,
-                                         int k, const mx4_experts* w_gu, const mx4_experts* w_dn,
-                                         float alpha, float limit, int32_t* ids, float* w,
-                                         int32_t* counts, int32_t* basep, int32_t* row_tok,
-                                         int32_t* pos, uint16_t* h, float* d, float* y,
-                                         uint32_t* ws, int max_workgroups, void* stream) {
+namespace {
+
+// Library-held workspace of mx4_moe_decode_persistent_static. A file-scope device array exists
+// once on every GPU the library runs on, each copy at its own device address; host code uses
+// only that address (from hipGetSymbolAddress, once per device), never the array's name.
+static __device__ __align__(256) uint32_t scratch[MOE_DECODE_WS_WORDS];
+static_assert(moe::kLyGo + moe::kLyLine * moe::kLyGroups <= MOE_DECODE_WS_WORDS,
+              "the layer kernel's counters fit the workspace");
+
+std::mutex g_scratch_mu;
+uint32_t* g_scratch[moe::kMaxDevices];   // device address of `scratch`, per device
+
+// This device's copy of `scratch` (looked up on the first call on the device), or NULL.
+uint32_t* scratch_ptr() {
+  const int slot = moe::device_slot();
+  if (slot < 0) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[slot]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[slot] = static_cast<uint32_t*>(p);
+  }
+  return g_scratch[slot];
+}
+
+// Zero fill of n words (a kernel, not a memset node: callers may capture the call in a graph).
+__global__ void __launch_bounds__(256) fill_zero_u32(uint32_t* __restrict__ p, int n) {
+  for (int i = (int)(blockIdx.x * blockDim.x + threadIdx.x); i < n; i += (int)(gridDim.x * blockDim.x))
+    p[i] = 0u;
+}
+
+// Shared body of both entry points. ws: the caller's workspace, or NULL for the library's own
+// (zeroed before the layer kernel on every call that launches it).
+int decode_persistent(const float* logits, const uint16_t* x, int64_t T, int E, int k,
+                      const mx4_experts* w_gu, const mx4_experts* w_dn, float alpha, float limit,
+                      int32_t* ids, float* w, int32_t* counts, int32_t* basep, int32_t* row_tok,
+                      int32_t* pos, uint16_t* h, float* d, float* y, uint32_t* ws,
+                      int max_workgroups, void* stream) {
+  const bool own_ws = ws == nullptr;
+
   if (!logits || !x || !w_gu || !w_dn || !ids || !w || !counts || !basep || !row_tok || !pos ||
-      !h || !y || !ws || !w_gu->q || !w_gu->s || !w_dn->q || !w_dn->s || T < 1 || E < 1 ||
+      !h || !y || !w_gu->q || !w_gu->s || !w_dn->q || !w_dn->s || T < 1 || E < 1 ||
       k < 1 || k > E || k > MOE_MAX_K || max_workgroups < 0)
     return MOE_EINVAL;
   if (T > MOE_DECODE_MAX_T || E > MOE_MAX_E || k > MOE_DECODE_MAX_K) return MOE_ESHAPE;
@@ -662,8 +698,40 @@ extern "C" int mx4_moe_decode_persistent(const float* logits, const uint16_t* x,
   a.h = h;
   a.d = d;
   a.y = y;
+  if (own_ws) {
+    ws = scratch_ptr();
+    if (!ws) return MOE_ELAUNCH;
+    moe::launch(fill_zero_u32, dim3(1), dim3(256), 0, (hipStream_t)stream, ws,
+                (int)MOE_DECODE_WS_WORDS);
+    if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
+  }
   a.ws = ws;
   moe::launch(moe::decode_layer_kernel, dim3((unsigned)G), dim3(moe::kLyThreads), lds,
               (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" int mx4_moe_decode_persistent(const float* logits, const uint16_t* x, int64_t T, int E,
+                                         int k, const mx4_experts* w_gu, const mx4_experts* w_dn,
+                                         float alpha, float limit, int32_t* ids, float* w,
+                                         int32_t* counts, int32_t* basep, int32_t* row_tok,
+                                         int32_t* pos, uint16_t* h, float* d, float* y,
+                                         uint32_t* ws, int max_workgroups, void* stream) {
+  if (!ws) return MOE_EINVAL;
+  return decode_persistent(logits, x, T, E, k, w_gu, w_dn, alpha, limit, ids, w, counts, basep,
+                           row_tok, pos, h, d, y, ws, max_workgroups, stream);
+}
+
+extern "C" int mx4_moe_decode_persistent_static(const float* logits, const uint16_t* x, int64_t T,
+                                                int E, int k, const mx4_experts* w_gu,
+                                                const mx4_experts* w_dn, float alpha,
+                                                float limit, int32_t* ids, float* w,
+                                                int32_t* counts, int32_t* basep,
+                                                int32_t* row_tok, int32_t* pos, uint16_t* h,
+                                                float* d, float* y, int max_workgroups,
+                                                void* stream) {
+  return decode_persistent(logits, x, T, E, k, w_gu, w_dn, alpha, limit, ids, w, counts, basep,
+                           row_tok, pos, h, d, y, nullptr, max_workgroups, stream);
 }

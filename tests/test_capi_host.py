@@ -29,6 +29,13 @@ def test_library_loads_and_exports_every_declared_function():
         assert hasattr(L, name), name
 
 
+def test_every_export_has_a_ctypes_signature():
+    L = _lib.lib()
+    for name in _lib.EXPORTS:
+        fn = getattr(L, name)
+        assert fn.argtypes is not None and fn.restype is not None, name
+
+
 def test_strerror_covers_every_status():
     for st in range(5):
         assert _lib.strerror(st) and _lib.strerror(st) != "unknown status"
