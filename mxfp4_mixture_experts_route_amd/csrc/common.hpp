@@ -77,6 +77,27 @@ __host__ __device__ __forceinline__ size_t chunked_block(int e, int n, int kb, i
 // Bytes per scale row of the chunked layout: the row's KB scale bytes padded to 16.
 __host__ __device__ __forceinline__ int scale_row_bytes(int KB) { return (KB + 15) & ~15; }
 
+// Four bias seeds of a 16-row MFMA tile, through the scalar cache: lane (lr, lg) gets rows
+// 4lg..4lg+3 of rows lo[0..7] (tile rows 0-7) and hi[0..7] (tile rows 8-15). lo and hi must be the
+// same on every lane (they are made so). A scalar load is not counted by the vector-memory
+// counter, so a wavefront that waits for its weight chunks in issue order never waits for its
+// seeds behind them (a vector load of the seeds, issued after the routing, arrives behind the
+// whole weight flood of the launch).
+__device__ __forceinline__ void scalar_seed16(const float* lo, const float* hi, float (&b4)[4]) {
+  typedef const __attribute__((address_space(4))) float* cfp;
+  const cfp cl = (cfp)lo, ch = (cfp)hi;
+  float g[8], u[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    g[i] = cl[i];
+    u[i] = ch[i];
+  }
+  const int lg = (int)(threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    b4[i] = lg == 0 ? g[i] : lg == 1 ? g[4 + i] : lg == 2 ? u[i] : u[4 + i];
+}
+
 // Scale operand of v_cvt_scalef32_* for an e8m0 byte e: the byte in the fp32 exponent field.
 // The instruction reads only that field and decodes it as e8m0 itself: 2^(e-127), with e = 0
 // giving 2^-127 (subnormal results kept) and e = 255 giving NaN; checked on gfx950 against the

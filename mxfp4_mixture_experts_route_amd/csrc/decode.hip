@@ -100,7 +100,8 @@ __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
   const int C = (KB + kChunkBlocks - 1) / kChunkBlocks;
   const int tid = (int)threadIdx.x;
   const int nthreads = (int)blockDim.x;
-  const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
   const int F = N >> 1;
   const int t = rho / k, slot = rho - t * k;
   const uint32_t row_bytes = (uint32_t)K * 2;
@@ -111,8 +112,10 @@ __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
   // would compute the same pick. For E <= 64 the logits row comes by LDS-DMA too, right after
   // the copy, so one wait lands both, and the rank reads it from LDS.
   lds_dma_copy(x + (size_t)t * K, row_bytes, xs, wave, nthreads >> 6);
-  __builtin_amdgcn_sched_barrier(0);
   const size_t zoff = ((size_t)row_bytes + 1023) & ~(size_t)1023;
+  // LDS after the row: a zero block, then 1 KB per wavefront (K-part sums)
+  if (tid < 4) *reinterpret_cast<uint4*>(xs + zoff + tid * 16) = make_uint4(0u, 0u, 0u, 0u);
+  __builtin_amdgcn_sched_barrier(0);
   // wavefront 0's 1 KB: the logits row, the rank keys at +256, the pick at +768
   uint8_t* const slot0 = xs + zoff + 64;
   int* const pick = reinterpret_cast<int*>(slot0 + 768);
@@ -136,7 +139,9 @@ __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
     }
     if (lane == 0) *pick = e0;
   }
-  __syncthreads();   // the pick is published (and every wavefront's share of the copy landed)
+  // every wavefront's share of the row copy has landed; the pick and the zero block are written
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
   // the top-k order is total (route_core.hpp), so the pick is an expert of [0, E) whatever the
   // logits hold; it is clamped all the same, as an id outside would address memory outside the
   // weight stack
@@ -156,22 +161,18 @@ __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
   const int n = row_of(lr, valid);
   Mx4Wave<SEG> ws;
   ws.init(q, s, e, n, valid, N, K, ce);
-  float b4[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bool ok;
-    const int nn = row_of(4 * lg + i, ok);
-    b4[i] = (ok && bias && part == 0) ? bias[(size_t)e * N + nn] : 0.0f;
-  }
+  // bias seeds (gate rows j..j+7, up rows F+j..F+j+7; F % 8 == 0, so a unit is whole or past F)
+  float b4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int ju = __builtin_amdgcn_readfirstlane(unit * 8);
+  const int eu = __builtin_amdgcn_readfirstlane(e);
+  if (bias && part == 0 && ju < F)
+    scalar_seed16(bias + (size_t)eu * N + ju, bias + (size_t)eu * N + F + ju, b4);
   ws.load_segment(cb);
 
-  // 3. zero block after the staged row; partial sums of the K parts after it
-  const size_t zero_off = ((size_t)row_bytes + 1023) & ~(size_t)1023;
-  if (tid < 4) *reinterpret_cast<uint4*>(xs + zero_off + tid * 16) = make_uint4(0u, 0u, 0u, 0u);
-  const uint8_t* xzero = xs + zero_off;
-  f32x4_t* red = reinterpret_cast<f32x4_t*>(xs + zero_off + 64);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(SEG + SEG / 4));   // the LDS-DMA copy has landed
-  __syncthreads();
+  // 3. the zero block after the staged row, then the partial sums of the K parts (all written
+  // or landed before the barrier above: the chunks run as their bytes arrive)
+  const uint8_t* xzero = xs + zoff;
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(xs + zoff + 64);
 
   // 4. one B column (the token); K segments; K parts meet in LDS
   f32x4_t acc = {b4[0], b4[1], b4[2], b4[3]};
@@ -214,16 +215,19 @@ decode_gate_up_kernel(const float* __restrict__ logits, const uint16_t* __restri
                       int ksplit, int32_t* __restrict__ ids, float* __restrict__ w,
                       int32_t* __restrict__ counts, int32_t* __restrict__ basep,
                       int32_t* __restrict__ row_tok, int32_t* __restrict__ pos,
-                      uint16_t* __restrict__ h) {
+                      uint16_t* __restrict__ h, int gx) {
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
-  const int R = T * k;
-  if ((int)blockIdx.y == R) {
-    if (blockIdx.x == 0) decode_bookkeeping(logits, T, E, k, ids, w, counts, basep, row_tok, pos);
+  // block 0 (dispatched first, so it never waits for a slot behind the items): the routing and
+  // the CSR for the caller; blocks 1..: the items, gx a routed row
+  if (blockIdx.x == 0) {
+    decode_bookkeeping(logits, T, E, k, ids, w, counts, basep, row_tok, pos);
     return;
   }
+  const int item = (int)blockIdx.x - 1;
+  const int rho = item / gx, bx = item - rho * gx;
   const int upw = ((int)blockDim.x >> 6) / ksplit;
-  gate_up_item<SEG>(logits, x, E, k, q, s, bias, N, K, alpha, limit, ksplit,
-                           (int)blockIdx.y, (int)blockIdx.x * upw, h, xs);
+  gate_up_item<SEG>(logits, x, E, k, q, s, bias, N, K, alpha, limit, ksplit, rho, bx * upw, h,
+                    xs);
 }
 
 template <int SEG>
@@ -237,7 +241,8 @@ decode_down_kernel(const uint16_t* __restrict__ h, int E, int k, const int32_t* 
   const int C = (KB + kChunkBlocks - 1) / kChunkBlocks;
   const int tid = (int)threadIdx.x;
   const int nthreads = (int)blockDim.x;
-  const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
   const int t = (int)blockIdx.y, unit = (int)blockIdx.x;
   const uint32_t row_bytes = (uint32_t)F * 2;
 
@@ -255,11 +260,11 @@ decode_down_kernel(const uint16_t* __restrict__ h, int E, int k, const int32_t* 
   const int n = unit * 16 + lr;
   Mx4Wave<SEG> ws;
   ws.init(q, s, e, n, n < D, D, F, ce);
-  float b4[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int nn = unit * 16 + 4 * lg + i;
-    b4[i] = (nn < D && bias && part == 0) ? bias[(size_t)e * D + nn] : 0.0f;
+  // bias seeds (rows unit*16..+15 are all inside D: D % 16 == 0)
+  float b4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (bias && part == 0) {
+    const float* br = bias + (size_t)__builtin_amdgcn_readfirstlane(e) * D + unit * 16;
+    scalar_seed16(br, br + 8, b4);
   }
   ws.load_segment(cb);
 
@@ -371,10 +376,11 @@ int moe_launch_decode_two(const float* logits, const uint16_t* x, int64_t T, int
       (int64_t)D * (F / 32) * 16 >= ((int64_t)1 << 31))
     return MOE_ESHAPE;
 
-  const dim3 g1((unsigned)((units1 + upw1 - 1) / upw1), (unsigned)(R + 1));
+  const int gx1 = (units1 + upw1 - 1) / upw1;
+  const dim3 g1((unsigned)(1 + gx1 * R));
   moe::launch(moe::decode_gate_up_kernel<moe::kGvSeg>, g1, dim3(64 * waves1), lds1, st, logits, x,
               (int)T, E, k, w_gu->q, w_gu->s, w_gu->bias, N, D, alpha, limit, ks1, ids, w, counts,
-              basep, row_tok, pos, h);
+              basep, row_tok, pos, h, gx1);
   if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
   const dim3 g2((unsigned)((D + 15) / 16), (unsigned)T);
   moe::launch(moe::decode_down_kernel<moe::kGvSeg>, g2, dim3(64 * waves2), lds2, st, h, E, k, ids, w,

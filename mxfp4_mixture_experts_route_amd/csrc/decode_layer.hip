@@ -323,22 +323,19 @@ decode_layer_kernel(LyArgs a) {
   }
   first_e = min(max(first_e, 0), a.E - 1);
 
-  // 3. every wavefront issues the loads of its first unit, bias seeds first: vector loads
-  // complete in issue order, so a seed loaded after the weights would hold the first chunk
-  // until the last had arrived
+  // 3. every wavefront issues the loads of its first unit; its bias seeds come through the
+  // scalar cache, outside the in-order count of the weight loads
   LyRing un;   // this wavefront's weights (a gate_up unit or a down item)
   f32x4_t seed = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto gate_up_seed = [&](int u, int e) {
+  auto gate_up_seed = [&](int u, int e) {   // through the scalar cache (scalar_seed16)
     const int t = u / a.Ut;
-    const int j = (u - t * a.Ut) % a.U1;
+    const int j = __builtin_amdgcn_readfirstlane(((u - t * a.Ut) % a.U1) * 8);
     f32x4_t sd = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (a.gb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {   // lane (lr, lg) ends with rows 4lg..4lg+3 of column lr
-        const int r16 = 4 * lg + i;
-        const int jj = j * 8 + (r16 & 7);
-        sd[i] = a.gb[(size_t)e * a.N + (r16 < 8 ? jj : F + jj)];   // jj < F: F % 8 == 0
-      }
+    if (a.gb) {   // j + 8 <= F: F % 8 == 0
+      const float* br = a.gb + (size_t)__builtin_amdgcn_readfirstlane(e) * a.N + j;
+      float b4[4];
+      scalar_seed16(br, br + F, b4);
+      sd = f32x4_t{b4[0], b4[1], b4[2], b4[3]};
     }
     return sd;
   };
@@ -349,14 +346,14 @@ decode_layer_kernel(LyArgs a) {
     un.init(a.gq, a.gs, e, lr < 8 ? jj : F + jj, true, a.N, D, 0, C1);
     un.start();
   };
-  auto down_seed = [&](int tile, int e) {
+  auto down_seed = [&](int tile, int e) {   // the bias seeds half 0's sums; D % 16 == 0
     f32x4_t sd = {0.0f, 0.0f, 0.0f, 0.0f};
-    if ((wave & 1) == 0 && a.db) {          // the bias seeds half 0's sums
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int nn = tile * 16 + 4 * lg + i;
-        sd[i] = nn < D ? a.db[(size_t)e * D + nn] : 0.0f;
-      }
+    if ((wave & 1) == 0 && a.db) {
+      const float* br =
+          a.db + (size_t)__builtin_amdgcn_readfirstlane(e) * D + __builtin_amdgcn_readfirstlane(tile) * 16;
+      float b4[4];
+      scalar_seed16(br, br + 8, b4);
+      sd = f32x4_t{b4[0], b4[1], b4[2], b4[3]};
     }
     return sd;
   };
