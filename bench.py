@@ -306,11 +306,11 @@ def router_us(moe, torch, layers, wl, reps, sleep_cycles):
     g = torch.Generator(device="cpu").manual_seed(99)
     wr = (torch.randn((wl.E, wl.dim), generator=g) / wl.dim ** 0.5).to(torch.bfloat16).cuda()
     br = (torch.randn(wl.E, generator=g) * 0.1).cuda()
-    sync = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(moe.MOE_ROUTER_WS_WORDS, dtype=torch.int32, device="cuda")
 
     def call(L):
         c = L.csr
-        moe.moe_router(L.x, wr, br, wl.k, wl.tile_m, sync, mpad_max=L.mpad, want_logits=False,
+        moe.moe_router(L.x, wr, br, wl.k, wl.tile_m, ws, mpad_max=L.mpad, want_logits=False,
                        out={"ids": L.ids, "w": L.w, "counts": c[0], "basep": c[1],
                             "row_tok": c[2], "pos": c[3]})
     return kernel_times_us(moe, torch, layers, call, 1, reps, sleep_cycles)[0]

@@ -220,6 +220,7 @@ int mx4_moe_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const 
                  int act, float alpha, float limit, void* out, void* stream);
 
 #define MOE_ROUTER_MAX_ROUTED 16384  /* T*k of one moe_router call */
+#define MOE_ROUTER_WS_WORDS 16448    /* u32 workspace words of moe_router */
 
 /*
  * The router projection and the routing front of the chain in one launch: the step before the
@@ -231,21 +232,25 @@ int mx4_moe_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const 
  *   counts, basep, row_tok, pos = moe_bucket of those ids with tile_m and mpad_max
  *   x     bf16 [T][D];  w_r bf16 [E][D];  b_r f32 [E] or NULL.
  *   logits f32 [T][E] out, or NULL (then not written).
- *   sync  u32 [1] device workspace owned by the caller: zero before the first call; every call
- *         leaves it zero. The workgroup that finishes last builds the CSR, found by counting
- *         on this word, so calls that can run concurrently need distinct words.
- * Cost: the CSR is built by one workgroup, in time proportional to E * T / 64 steps per
- * wavefront; for large E * T the separate moe_route_topk + moe_bucket (one workgroup per
- * expert) spread that work wider.
+ *   ws    u32 [MOE_ROUTER_WS_WORDS] device workspace owned by the caller: zero before the first
+ *         call, then left to the library (every call leaves word 0, its completion counter,
+ *         zero; the rest holds the last call's partial logits). The workgroup that finishes last
+ *         builds the CSR, found by counting on word 0, so calls that can run concurrently need
+ *         distinct workspaces.
+ * For T <= 16 and E <= 256 the reduction over D is split over up to 48 workgroups, whose
+ * partial logits are summed in a fixed order (results are deterministic; they differ from the
+ * one-workgroup sum only by fp32 association). Cost: the CSR is built by one workgroup, in time
+ * proportional to E * T / 64 steps per wavefront; for large E * T the separate moe_route_topk +
+ * moe_bucket (one workgroup per expert) spread that work wider.
  * Errors: MOE_EINVAL for NULL pointers (other than b_r, logits), T, D or E < 1, k < 1,
  *         k > min(E, MOE_MAX_K); MOE_ESHAPE for D % 32 != 0, T*k > MOE_ROUTER_MAX_ROUTED,
  *         E > MOE_MAX_E, tile_m outside [1, MOE_MAX_TILE_M], mpad_max < moe_mpad_max(T, k, E,
- *         tile_m), x or W_r of 2 GB or more; MOE_EALIGN for x or w_r not 16-byte aligned;
- *         MOE_ELAUNCH.
+ *         tile_m), x or W_r of 2 GB or more; MOE_EALIGN for x or w_r not 16-byte aligned or ws
+ *         not 4-byte aligned; MOE_ELAUNCH.
  */
 int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b_r, int64_t T, int D,
                int E, int k, int tile_m, int64_t mpad_max, float* logits, int32_t* ids, float* w,
-               int32_t* counts, int32_t* basep, int32_t* row_tok, int32_t* pos, uint32_t* sync,
+               int32_t* counts, int32_t* basep, int32_t* row_tok, int32_t* pos, uint32_t* ws,
                void* stream);
 
 /*

@@ -24,6 +24,7 @@ EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_
            "moe_probe_mfma_bf16")
 MOE_DECODE_WS_WORDS = 544
 MOE_ROUTER_MAX_ROUTED = 16384
+MOE_ROUTER_WS_WORDS = 16448
 MOE_MX8_GEMM_MAX_K = 4096
 
 
@@ -226,11 +227,12 @@ def moe_route_topk(logits, k: int, ids=None, w=None, stream=None):
     return ids, w
 
 
-def moe_router(x, w_r, b_r, k: int, tile_m: int, sync, mpad_max: int | None = None,
+def moe_router(x, w_r, b_r, k: int, tile_m: int, ws, mpad_max: int | None = None,
                want_logits: bool = True, out=None, stream=None):
     """Router projection + top-k + bucket in one launch. x bf16 [T][D], w_r bf16 [E][D], b_r f32
-    [E] or None, sync a zeroed int32/uint32 device tensor of one element (left zero). Returns a
-    dict: logits (if want_logits), ids, w, counts, basep, row_tok, pos, mpad."""
+    [E] or None, ws an int32/uint32 device tensor of MOE_ROUTER_WS_WORDS elements, zero before
+    its first use and then left to the library (word 0 is left zero). Returns a dict: logits (if
+    want_logits), ids, w, counts, basep, row_tok, pos, mpad."""
     torch = _torch()
     _check(x, torch.bfloat16, "x")
     _check(w_r, torch.bfloat16, "w_r")
@@ -252,7 +254,7 @@ def moe_router(x, w_r, b_r, k: int, tile_m: int, sync, mpad_max: int | None = No
             o[key] = torch.empty(shape, dtype=dt, device=dev)
     _call("moe_router", _ptr(x), _ptr(w_r), _ptr(b_r), T, D, E, k, tile_m, mpad_max,
           _ptr(o.get("logits")), _ptr(o["ids"]), _ptr(o["w"]), _ptr(o["counts"]), _ptr(o["basep"]),
-          _ptr(o["row_tok"]), _ptr(o["pos"]), _ptr(sync), _stream(stream))
+          _ptr(o["row_tok"]), _ptr(o["pos"]), _ptr(ws), _stream(stream))
     o["mpad"] = mpad_max
     return o
 

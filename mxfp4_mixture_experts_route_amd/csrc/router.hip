@@ -16,10 +16,18 @@
 //  * top-k: one wavefront per token on the LDS logits row (the moe_route_topk code).
 //  * bucket: the CSR needs every token's ids, so the LAST workgroup to finish its tokens builds
 //    it: each workgroup stores its ids with device-scope atomic stores, waits for them to be
-//    acknowledged and increments a caller-provided counter; the one that brings it to the grid
-//    size reads every id with device-scope atomic loads, copies them into LDS, histograms them, scans the padded counts into basep, and compacts each expert's
-//    rows in ascending token order (each wavefront owns whole experts, one ballot per 64
-//    tokens), then resets the counter to zero. No workgroup ever waits for another.
+//    acknowledged and increments a counter in the caller's workspace; the one that brings it to
+//    the grid size reads every id with device-scope atomic loads, copies them into LDS,
+//    histograms them, scans the padded counts into basep, and compacts each expert's rows in
+//    ascending token order (each wavefront owns whole experts, one ballot per 64 tokens), then
+//    resets the counter to zero. No workgroup ever waits for another.
+//  * A few tokens (T <= 16, one token tile): the reduction is split over up to 48 workgroups of
+//    4 wavefronts instead (one workgroup alone would read all the router rows from one CU, at a
+//    small fraction of the chip's rate); their partial logits meet in the workspace, summed in
+//    split order by the workgroup that completes the count, which then routes and builds the
+//    CSR from its own LDS.
+#include <algorithm>
+
 #include "route_core.hpp"
 #include "launch.hpp"
 
@@ -28,6 +36,10 @@ namespace moe {
 constexpr int kRtWaves = 16;
 constexpr int kRtThreads = kRtWaves * kWave;
 constexpr int kRtTok = 16;   // tokens per workgroup
+constexpr int kSpWaves = 4;  // split kernel: wavefronts per workgroup
+constexpr int kSpThreads = kSpWaves * kWave;
+constexpr int kSpMaxSplit = 48;
+constexpr int kRtPartOff = 64;   // workspace words before the split kernel's partial logits
 
 // expert tiles and the K split of the logits stage
 __host__ __device__ inline int rt_tiles(int E) { return (E + 15) / 16; }
@@ -36,93 +48,97 @@ __host__ __device__ inline int rt_ksplit(int E) {
   return n >= kRtWaves ? 1 : kRtWaves / n;
 }
 // dynamic LDS: the logits stage's partial tiles, or the bucket's histogram, bases and ids
-__host__ inline size_t rt_lds_bytes(int E, int64_t R) {
-  const size_t p1 = (size_t)rt_ksplit(E) * kRtTok * E * sizeof(float);
+// after the tile's logits rows (row reads of the rank may run up to 63 floats past a row) or
+// the bucket's arrays: 512 B of rank keys per wavefront
+__host__ __device__ inline size_t rt_keys_off(size_t rows_bytes, int E, int64_t R) {
+  const size_t p1 = rows_bytes + kWave * sizeof(float);
   const size_t p2 = (size_t)(2 * E + R) * sizeof(int);
-  return p1 > p2 ? p1 : p2;
+  return ((p1 > p2 ? p1 : p2) + 15) & ~(size_t)15;
+}
+__host__ inline size_t rt_lds_bytes(int E, int64_t R) {
+  return rt_keys_off((size_t)rt_ksplit(E) * kRtTok * E * sizeof(float), E, R) +
+         (size_t)kRtWaves * kWave * sizeof(uint64_t);
+}
+// split kernel: the tile's logits rows, or the bucket's arrays; then the keys
+__host__ inline size_t sp_lds_bytes(int E, int64_t R) {
+  return rt_keys_off((size_t)kRtTok * E * sizeof(float), E, R) +
+         (size_t)kSpWaves * kWave * sizeof(uint64_t);
 }
 
-__global__ void __launch_bounds__(kRtThreads)
-router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-              const float* __restrict__ br, int T, int D, int E, int k, int tile_m,
-              int mpad_max, float* __restrict__ logits, int32_t* __restrict__ ids,
-              float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ basep,
-              int32_t* __restrict__ row_tok, int32_t* __restrict__ pos,
-              uint32_t* __restrict__ sync) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+// 16 x 16 logits tile of (16 experts from e_row0, 16 tokens from t0) over k steps [s0, s1) of
+// 32: MFMA with the router rows as A and the tokens as B; lane (lr, lg) ends with experts
+// e_row0 + 4lg..+3 of token t0 + lr. 8 steps per round, all 16 loads in flight before the
+// MFMAs; steps past s1, experts past E and tokens past T read zeros.
+__device__ __forceinline__ f32x4_t router_tile(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx,
+                                               int D, int E, int T, int e_row0, int t0, int s0,
+                                               int s1) {
+  const int lane = (int)(threadIdx.x & 63), lr = lane & 15, lg = lane >> 4;
+  const int e_row = e_row0 + lr;
+  const uint32_t ao = e_row < E ? ((uint32_t)e_row * D + 8 * lg) * 2 : kOOB;
+  const uint32_t bo = t0 + lr < T ? ((uint32_t)(t0 + lr) * D + 8 * lg) * 2 : kOOB;
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int sb = s0; sb < s1; sb += 8) {
+    u32x4_t a[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool ok = sb + i < s1;
+      a[i] = buf_load16(rw, ok ? ao : kOOB, (uint32_t)(sb + i) * 64);
+      b[i] = buf_load16(rx, ok ? bo : kOOB, (uint32_t)(sb + i) * 64);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bf16x8_t A, B;
+      __builtin_memcpy(&A, &a[i], 16);
+      __builtin_memcpy(&B, &b[i], 16);
+      if (i & 1)
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc1, 0, 0, 0);
+      else
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc0, 0, 0, 0);
+    }
+  }
+  return acc0 + acc1;
+}
+
+// The routing of tokens t0.. (at most 16) from their logits rows in LDS (part[tok][E]), then the
+// CSR by the workgroup that holds the last picks. counter: the caller's completion word when
+// several workgroups route (the one that completes the count builds the CSR from the ids in
+// memory), or NULL when this workgroup routes every token (the ids are in its LDS).
+// keys: 512 B of LDS per wavefront for the rank of an E <= 64 row (else unused).
+__device__ void router_tail(float* part, int T, int t0, int E, int k, int tile_m, int mpad_max,
+                            int32_t* __restrict__ ids, float* __restrict__ w,
+                            int32_t* __restrict__ counts, int32_t* __restrict__ basep,
+                            int32_t* __restrict__ row_tok, int32_t* __restrict__ pos,
+                            uint32_t* counter, int n_groups, uint8_t* smem, uint64_t* keys) {
   __shared__ int s_last;
-  __shared__ int s_ids[kRtTok * MOE_MAX_K];   // this workgroup's picks (the one-workgroup case)
+  __shared__ int s_ids[kRtTok * MOE_MAX_K];   // this workgroup's picks
   __shared__ int s_wave_tot[kRtWaves];
-  const int tid = (int)threadIdx.x;
+  const int tid = (int)threadIdx.x, nthreads = (int)blockDim.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 15, lg = lane >> 4;
-  const int t0 = (int)blockIdx.x * kRtTok;
-  const int ntiles = rt_tiles(E), ksplit = rt_ksplit(E);
-  const int KS = D >> 5;   // 32-wide k steps
-  float* part = reinterpret_cast<float*>(smem);   // [ksplit][kRtTok][E]
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), waves = nthreads >> 6;
 
-  // ---- logits of the workgroup's 16 tokens ----
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wr, (uint32_t)E * D * 2);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)T * D * 2);
-  for (int u = wave; u < ntiles * ksplit; u += kRtWaves) {
-    const int tile = u % ntiles, p = u / ntiles;
-    const int s0 = p * KS / ksplit, s1 = (p + 1) * KS / ksplit;
-    const int e_row = tile * 16 + lr;
-    const uint32_t ao = e_row < E ? ((uint32_t)e_row * D + 8 * lg) * 2 : kOOB;
-    const uint32_t bo = t0 + lr < T ? ((uint32_t)(t0 + lr) * D + 8 * lg) * 2 : kOOB;
-    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    // 8 k steps per round: all 16 loads in flight before the MFMAs (steps past s1 read zeros)
-    for (int sb = s0; sb < s1; sb += 8) {
-      u32x4_t a[8], b[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool ok = sb + i < s1;
-        a[i] = buf_load16(rw, ok ? ao : kOOB, (uint32_t)(sb + i) * 64);
-        b[i] = buf_load16(rx, ok ? bo : kOOB, (uint32_t)(sb + i) * 64);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        bf16x8_t A, B;
-        __builtin_memcpy(&A, &a[i], 16);
-        __builtin_memcpy(&B, &b[i], 16);
-        if (i & 1)
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc1, 0, 0, 0);
-        else
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc0, 0, 0, 0);
-      }
-    }
-    // lane holds experts tile*16 + 4*lg + i of token lr
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tile * 16 + 4 * lg + i;
-      if (e < E) part[((size_t)p * kRtTok + lr) * E + e] = acc0[i] + acc1[i];
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < kRtTok * E; i += kRtThreads) {
-    const int tok = i / E, e = i - tok * E;
-    float v = part[(size_t)tok * E + e];
-    for (int p = 1; p < ksplit; ++p) v += part[((size_t)p * kRtTok + tok) * E + e];
-    if (br) v += br[e];
-    part[(size_t)tok * E + e] = v;   // only this thread touches element (tok, e)
-    if (logits && t0 + tok < T) logits[(size_t)(t0 + tok) * E + e] = v;
-  }
-  __syncthreads();
-
-  // ---- top-k: wavefront w routes token t0 + w ----
-  if (t0 + wave < T) {
-    int my_id;
+  // ---- top-k: wavefront w routes tokens t0 + w, t0 + w + waves, ... ----
+  for (int tt = wave; tt < kRtTok && t0 + tt < T; tt += waves) {
+    int my_id = 0;
     float my_v;
-    wave_topk(part + (size_t)wave * E, E, k, my_id, my_v);
+    const float* row = part + (size_t)tt * E;
+    if (E <= kWave) {   // rank against the row's keys in LDS (row[lane] read for every lane)
+      const int rank = wave_rank_lds(row, keys + (size_t)wave * kWave, E);
+      for (int r = 0; r < k; ++r) {
+        const int id = rank_pick(rank, r);
+        if (lane == r) my_id = id;
+      }
+      my_v = row[min(max(my_id, 0), kWave - 1)];
+    } else {
+      wave_topk(row, E, k, my_id, my_v);
+    }
     // the ids are stored with device-scope atomic stores, which bypass the XCD's non-coherent
     // L2, so that another XCD's workgroup can read them
     const float wt = topk_weight(my_v, k);
     if (lane < k) {
-      __hip_atomic_store(ids + (size_t)(t0 + wave) * k + lane, my_id, __ATOMIC_RELAXED,
+      __hip_atomic_store(ids + (size_t)(t0 + tt) * k + lane, my_id, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-      w[(size_t)(t0 + wave) * k + lane] = wt;
-      s_ids[wave * k + lane] = my_id;
+      w[(size_t)(t0 + tt) * k + lane] = wt;
+      s_ids[tt * k + lane] = my_id;
     }
   }
 
@@ -131,14 +147,13 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
   // in; the one that completes the count reads the ids with device-scope atomic loads. (A
   // device-scope fence would also work but writes back and invalidates the whole L2, which
   // costs microseconds per workgroup.)
-  // (A grid of one workgroup is the last by itself and has every id in LDS already.)
-  const bool alone = gridDim.x == 1;
+  const bool alone = counter == nullptr;
   if (!alone) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     if (tid == 0)
-      s_last = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               gridDim.x - 1;
+      s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)n_groups - 1;
     __syncthreads();
     if (!s_last) return;
   } else {
@@ -149,16 +164,16 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
   int* hist = reinterpret_cast<int*>(smem);
   int* base = hist + E;
   int* idl = base + E;
-  for (int i = tid; i < E; i += kRtThreads) hist[i] = 0;
+  for (int i = tid; i < E; i += nthreads) hist[i] = 0;
   __syncthreads();
-  for (int i = tid; i < R; i += kRtThreads) {
+  for (int i = tid; i < R; i += nthreads) {
     const int id = alone ? s_ids[i]
                          : __hip_atomic_load(ids + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     idl[i] = id;
     if ((unsigned)id < (unsigned)E) atomicAdd(&hist[id], 1);
   }
   __syncthreads();
-  // exclusive scan of the padded counts over the experts (E <= 1024: one per thread)
+  // exclusive scan of the padded counts over the experts (E <= nthreads: one per thread)
   const int cnt = tid < E ? hist[tid] : 0;
   const int padded = (cnt + tile_m - 1) / tile_m * tile_m;
   int incl = padded;
@@ -169,7 +184,7 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
   if (lane == 63) s_wave_tot[wave] = incl;
   __syncthreads();
   int before = 0, total = 0;
-  for (int v = 0; v < kRtWaves; ++v) {
+  for (int v = 0; v < waves; ++v) {
     if (v < wave) before += s_wave_tot[v];
     total += s_wave_tot[v];
   }
@@ -181,8 +196,27 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
   }
   if (tid == 0) basep[E] = total;
   __syncthreads();
-  // ordered compaction: wavefront v owns experts v, v + 16, ...
-  for (int e = wave; e < E; e += kRtWaves) {
+  if (alone) {
+    // every routed row at once: the CSR row of (t, s) follows the earlier tokens routed to the
+    // same expert (a token picks an expert at most once); then each expert's padding rows
+    for (int r = tid; r < R; r += nthreads) {
+      const int e = idl[r], t = r / k;
+      if ((unsigned)e >= (unsigned)E) continue;
+      int rank = 0;
+      for (int r2 = 0; r2 < t * k; ++r2) rank += idl[r2] == e;
+      pos[r] = base[e] + rank;
+      row_tok[base[e] + rank] = t0 + t;
+    }
+    for (int e = tid; e < E; e += nthreads) {
+      const int c = hist[e];
+      const int pe = (c + tile_m - 1) / tile_m * tile_m;
+      for (int j = c; j < pe; ++j) row_tok[base[e] + j] = -1;
+    }
+    for (int r = total + tid; r < mpad_max; r += nthreads) row_tok[r] = -1;   // ghost rows
+    return;
+  }
+  // ordered compaction: wavefront v owns experts v, v + waves, ...
+  for (int e = wave; e < E; e += waves) {
     const int b = base[e];
     int running = 0;
     for (int tt = 0; tt < T; tt += 64) {
@@ -202,9 +236,129 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const int pe = (running + tile_m - 1) / tile_m * tile_m;
     for (int r = b + running + lane; r < b + pe; r += 64) row_tok[r] = -1;   // padding rows
   }
-  for (int r = total + tid; r < mpad_max; r += kRtThreads) row_tok[r] = -1;   // ghost rows
+  for (int r = total + tid; r < mpad_max; r += nthreads) row_tok[r] = -1;   // ghost rows
   if (tid == 0 && !alone)   // ready for the next call
-    __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroups of 16 wavefronts each take 16 tokens over the whole reduction.
+__global__ void __launch_bounds__(kRtThreads)
+router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+              const float* __restrict__ br, int T, int D, int E, int k, int tile_m,
+              int mpad_max, float* __restrict__ logits, int32_t* __restrict__ ids,
+              float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ basep,
+              int32_t* __restrict__ row_tok, int32_t* __restrict__ pos,
+              uint32_t* __restrict__ ws) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int t0 = (int)blockIdx.x * kRtTok;
+  const int ntiles = rt_tiles(E), ksplit = rt_ksplit(E);
+  const int KS = D >> 5;   // 32-wide k steps
+  float* part = reinterpret_cast<float*>(smem);   // [ksplit][kRtTok][E]
+
+  // ---- logits of the workgroup's 16 tokens ----
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wr, (uint32_t)E * D * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)T * D * 2);
+  for (int u = wave; u < ntiles * ksplit; u += kRtWaves) {
+    const int tile = u % ntiles, p = u / ntiles;
+    const f32x4_t acc = router_tile(rw, rx, D, E, T, tile * 16, t0, p * KS / ksplit,
+                                    (p + 1) * KS / ksplit);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tile * 16 + 4 * lg + i;
+      if (e < E) part[((size_t)p * kRtTok + lr) * E + e] = acc[i];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kRtTok * E; i += kRtThreads) {
+    const int tok = i / E, e = i - tok * E;
+    float v = part[(size_t)tok * E + e];
+    for (int p = 1; p < ksplit; ++p) v += part[((size_t)p * kRtTok + tok) * E + e];
+    if (br) v += br[e];
+    part[(size_t)tok * E + e] = v;   // only this thread touches element (tok, e)
+    if (logits && t0 + tok < T) logits[(size_t)(t0 + tok) * E + e] = v;
+  }
+  __syncthreads();
+  uint64_t* const keys = reinterpret_cast<uint64_t*>(
+      smem + rt_keys_off((size_t)ksplit * kRtTok * E * sizeof(float), E, (int64_t)T * k));
+  router_tail(part, T, t0, E, k, tile_m, mpad_max, ids, w, counts, basep, row_tok, pos,
+              gridDim.x == 1 ? nullptr : ws, (int)gridDim.x, smem, keys);
+}
+
+// A few tokens (T <= 16, E <= 256): the reduction split over `nsplit` small workgroups, so that
+// the router rows stream from many CUs at once (one CU alone reads them at a fraction of the
+// chip's rate). Workgroup s takes k steps [s*KS/nsplit, (s+1)*KS/nsplit) of every expert tile
+// and stores its partial logits [T][E] in the workspace (device-scope stores); the workgroup
+// that completes the count sums the partials in split order, adds the bias and routes every
+// token, then builds the CSR from its own LDS.
+__global__ void __launch_bounds__(kSpThreads)
+router_split_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                    const float* __restrict__ br, int T, int D, int E, int k, int tile_m,
+                    int mpad_max, float* __restrict__ logits, int32_t* __restrict__ ids,
+                    float* __restrict__ w, int32_t* __restrict__ counts,
+                    int32_t* __restrict__ basep, int32_t* __restrict__ row_tok,
+                    int32_t* __restrict__ pos, uint32_t* __restrict__ ws, int nsplit) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_last;
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int s = (int)blockIdx.x;
+  const int KS = D >> 5;
+  float* const partg = reinterpret_cast<float*>(ws + kRtPartOff);   // [nsplit][T][E]
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wr, (uint32_t)E * D * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)T * D * 2);
+  for (int tile = wave; tile < rt_tiles(E); tile += kSpWaves) {
+    const f32x4_t acc = router_tile(rw, rx, D, E, T, tile * 16, 0, s * KS / nsplit,
+                                    (s + 1) * KS / nsplit);
+    if (lr < T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = tile * 16 + 4 * lg + i;
+        if (e < E)
+          __hip_atomic_store(partg + ((size_t)s * T + lr) * E + e, acc[i], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the partials are acknowledged
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(ws, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)nsplit - 1;
+  __syncthreads();
+  if (!s_last) return;
+  // the last workgroup: logits = sum of the partials in split order, then the bias. The
+  // partials are read with the device-coherent bit (sc1, as the device-scope stores that wrote
+  // them), as plain loads: all in flight at once (atomic loads would be issued one at a time)
+  float* part = reinterpret_cast<float*>(smem);   // [kRtTok][E]
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(partg, (uint32_t)nsplit * T * E * 4);
+  for (int i = tid; i < T * E; i += kSpThreads) {
+    const int tok = i / E, e = i - tok * E;
+    float pv[kSpMaxSplit];
+#pragma unroll
+    for (int s2 = 0; s2 < kSpMaxSplit; ++s2)
+      pv[s2] = s2 < nsplit ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                 rp, (uint32_t)(((s2 * T + tok) * E + e) * 4), 0, 16))
+                           : 0.0f;
+    float v = 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < kSpMaxSplit; ++s2)
+      if (s2 < nsplit) v += pv[s2];
+    if (br) v += br[e];
+    part[(size_t)tok * E + e] = v;
+    if (logits) logits[(size_t)tok * E + e] = v;
+  }
+  if (tid == 0) __hip_atomic_store(ws, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  uint64_t* const keys = reinterpret_cast<uint64_t*>(
+      smem + rt_keys_off((size_t)kRtTok * E * sizeof(float), E, (int64_t)T * k));
+  router_tail(part, T, 0, E, k, tile_m, mpad_max, ids, w, counts, basep, row_tok, pos, nullptr,
+              1, smem, keys);
 }
 
 }  // namespace moe
@@ -212,8 +366,8 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
 extern "C" int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b_r, int64_t T,
                           int D, int E, int k, int tile_m, int64_t mpad_max, float* logits,
                           int32_t* ids, float* w, int32_t* counts, int32_t* basep,
-                          int32_t* row_tok, int32_t* pos, uint32_t* sync, void* stream) {
-  if (!x || !w_r || !ids || !w || !counts || !basep || !row_tok || !pos || !sync || T < 1 ||
+                          int32_t* row_tok, int32_t* pos, uint32_t* ws, void* stream) {
+  if (!x || !w_r || !ids || !w || !counts || !basep || !row_tok || !pos || !ws || T < 1 ||
       D < 1 || E < 1 || k < 1 || k > E || k > MOE_MAX_K)
     return MOE_EINVAL;
   if (E > MOE_MAX_E || D % 32 != 0 || T * k > MOE_ROUTER_MAX_ROUTED || tile_m < 1 ||
@@ -222,7 +376,22 @@ extern "C" int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b
     return MOE_ESHAPE;
   const int64_t need = moe_mpad_max(T, k, E, tile_m);
   if (mpad_max < need || mpad_max > 0x7FFFFFFFLL) return MOE_ESHAPE;
-  if ((((uintptr_t)x) & 15) || (((uintptr_t)w_r) & 15)) return MOE_EALIGN;
+  if ((((uintptr_t)x) & 15) || (((uintptr_t)w_r) & 15) || (((uintptr_t)ws) & 3))
+    return MOE_EALIGN;
+  // a few tokens: the reduction split over workgroups whose partials fit the workspace
+  const int KS = D / 32;
+  int nsplit = 0;
+  if (T <= moe::kRtTok && E <= moe::kSpThreads) {
+    const int64_t cap = (MOE_ROUTER_WS_WORDS - moe::kRtPartOff) / (T * (int64_t)E);
+    nsplit = (int)std::min<int64_t>(std::min<int64_t>(cap, KS), moe::kSpMaxSplit);
+  }
+  if (nsplit >= 2) {
+    moe::launch(moe::router_split_kernel, dim3((unsigned)nsplit), dim3(moe::kSpThreads),
+                (unsigned)moe::sp_lds_bytes(E, T * k), (hipStream_t)stream, x, w_r, b_r, (int)T, D,
+                E, k, tile_m, (int)mpad_max, logits, ids, w, counts, basep, row_tok, pos, ws,
+                nsplit);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+  }
   const size_t lds = moe::rt_lds_bytes(E, T * k);
   static bool lds_attr_set[moe::kMaxDevices] = {};   // > 64 KB of LDS: opt in once per device
   const int dslot = moe::device_slot();
@@ -236,6 +405,6 @@ extern "C" int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b
   const int64_t blocks = (T + moe::kRtTok - 1) / moe::kRtTok;
   moe::launch(moe::router_kernel, dim3((unsigned)blocks), dim3(moe::kRtThreads), (unsigned)lds,
               (hipStream_t)stream, x, w_r, b_r, (int)T, D, E, k, tile_m, (int)mpad_max, logits,
-              ids, w, counts, basep, row_tok, pos, sync);
+              ids, w, counts, basep, row_tok, pos, ws);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

@@ -228,13 +228,14 @@ def test_router_argument_checks():
     f = _lib.lib().moe_router
 
     def call(x=FAKE, w_r=FAKE, b_r=None, T=4, D=64, E=8, k=2, tile_m=4, mpad=64, logits=None,
-             sync=FAKE):
+             ws=FAKE):
         return f(x, w_r, b_r, T, D, E, k, tile_m, mpad, logits, FAKE, FAKE, FAKE, FAKE, FAKE,
-                 FAKE, sync, None)
+                 FAKE, ws, None)
 
     assert call(x=None) == _lib.MOE_EINVAL
     assert call(w_r=None) == _lib.MOE_EINVAL
-    assert call(sync=None) == _lib.MOE_EINVAL
+    assert call(ws=None) == _lib.MOE_EINVAL
+    assert call(ws=ctypes.c_void_p(0x1002)) == _lib.MOE_EALIGN
     assert call(T=0) == _lib.MOE_EINVAL
     assert call(k=9) == _lib.MOE_EINVAL
     assert call(k=17, E=32) == _lib.MOE_EINVAL

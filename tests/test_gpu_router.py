@@ -3,7 +3,9 @@ through the C ABI.
 
 Protocol: the fp32 logits within |gpu - ref| <= 1e-3 * S + 1e-5 of oracle.router_logits; the
 routing decisions taken on the GPU's own fp32 logits (ids, weights) and the CSR built from the
-GPU's ids equal the oracle's route_topk and bucket bit for bit; the sync word is left zero.
+GPU's ids equal the oracle's route_topk and bucket bit for bit; the workspace's counter word is
+left zero. A few tokens (T <= 16, E <= 256) take the split-reduction kernel, more the
+one-workgroup-per-16-tokens kernel; both are covered, and one workspace serves both in turn.
 """
 import numpy as np
 import pytest
@@ -34,16 +36,21 @@ def router_case(seed, T, D, E, bias=True, dup_rows=()):
     return x, w, b
 
 
-def check_router(x, w, b, k, tile_m, want_logits=True, sync=None):
+def new_ws():
+    import torch
+    return torch.zeros(moe.MOE_ROUTER_WS_WORDS, dtype=torch.int32, device="cuda")
+
+
+def check_router(x, w, b, k, tile_m, want_logits=True, ws=None):
     import torch
     T, D = x.shape
     E = w.shape[0]
-    if sync is None:
-        sync = torch.zeros(1, dtype=torch.int32, device="cuda")
-    out = moe.moe_router(bf16_dev(x), bf16_dev(w), None if b is None else dev(b), k, tile_m, sync,
+    if ws is None:
+        ws = new_ws()
+    out = moe.moe_router(bf16_dev(x), bf16_dev(w), None if b is None else dev(b), k, tile_m, ws,
                          want_logits=True)
     torch.cuda.synchronize()
-    assert int(host(sync)[0]) == 0, "sync word not left zero"
+    assert int(host(ws)[0]) == 0, "counter word not left zero"
     lg = host(out["logits"])
     ref, S = oracle.router_logits(x, w, b)
     assert_within(lg, ref, S, "router logits")
@@ -59,6 +66,14 @@ def check_router(x, w, b, k, tile_m, want_logits=True, sync=None):
 
 CASES = {
     "decode_T1": dict(T=1, D=2880, E=32, k=4, tile_m=1),
+    # split reduction: every token in one tile, E up to 256, ragged E and D
+    "split_T16_E256": dict(T=16, D=2880, E=256, k=8, tile_m=16),
+    "split_T3_E21": dict(T=3, D=96, E=21, k=3, tile_m=4),
+    "split_T7_E128_D64": dict(T=7, D=64, E=128, k=4, tile_m=1),
+    "split_T1_E1": dict(T=1, D=32, E=1, k=1, tile_m=1),
+    # just past the split kernel's limits: the one-workgroup-per-tile kernel
+    "T17_E32": dict(T=17, D=2880, E=32, k=4, tile_m=1),
+    "T2_E257": dict(T=2, D=64, E=257, k=4, tile_m=1),
     "pp512": dict(T=512, D=2880, E=32, k=4, tile_m=16),
     "ragged": dict(T=37, D=96, E=8, k=2, tile_m=7),
     "wide_E128": dict(T=100, D=256, E=128, k=4, tile_m=16),
@@ -85,11 +100,13 @@ def test_router_without_bias_and_ties():
     assert np.array_equal(lg[:, 3], lg[:, 9]) and np.array_equal(lg[:, 4], lg[:, 5])
 
 
-def test_router_sync_word_reused_across_calls():
-    import torch
-    sync = torch.zeros(1, dtype=torch.int32, device="cuda")
+def test_router_workspace_reused_across_calls():
+    ws = new_ws()
     x, w, b = router_case(7, 100, 64, 32)
     for _ in range(3):
-        check_router(x, w, b, 4, 16, sync=sync)
-    x2, w2, b2 = router_case(8, 3, 64, 32)     # a smaller call on the same word
-    check_router(x2, w2, b2, 2, 4, sync=sync)
+        check_router(x, w, b, 4, 16, ws=ws)
+    x2, w2, b2 = router_case(8, 3, 64, 32)     # a smaller call (split kernel) on the same words
+    a = check_router(x2, w2, b2, 2, 4, ws=ws)
+    b_ = check_router(x2, w2, b2, 2, 4, ws=ws)   # deterministic: the same partial-sum order
+    assert np.array_equal(host(a["logits"]).view(np.uint32), host(b_["logits"]).view(np.uint32))
+    check_router(x, w, b, 4, 16, ws=ws)        # and back to the multi-workgroup kernel
