@@ -15,12 +15,18 @@
 //    E read zeros.
 //  * top-k: one wavefront per token on the LDS logits row (the moe_route_topk code).
 //  * bucket: the CSR needs every token's ids, so the LAST workgroup to finish its tokens builds
-//    it: each workgroup stores its ids with device-scope atomic stores, waits for them to be
-//    acknowledged and increments a counter in the caller's workspace; the one that brings it to
-//    the grid size reads every id with device-scope atomic loads, copies them into LDS,
-//    histograms them, scans the padded counts into basep, and compacts each expert's rows in
-//    ascending token order (each wavefront owns whole experts, one ballot per 64 tokens), then
-//    resets the counter to zero. No workgroup ever waits for another.
+//    it: each workgroup stores its ids, and for each pick the number of earlier picks of the
+//    same expert among its own 16 tokens (into pos[]), with device-scope stores, waits for them
+//    to be acknowledged and increments a counter in the caller's workspace; the one that brings
+//    it to the grid size resets the counter, reads every id and in-group count with
+//    device-coherent loads (all in flight), histograms the picks per group in LDS, scans the
+//    histograms over the groups and the padded counts over the experts, and places every pick
+//    at base[e] + (picks of e in earlier groups) + (its in-group count). When the per-group table
+//    does not fit its LDS budget, each wavefront instead sweeps all ids for whole experts in
+//    ascending token order (one ballot per 64 tokens). No workgroup ever waits for another. The
+//    tail is inlined into each kernel so that its LDS and global accesses keep their address
+//    spaces (as a called function they become flat accesses, whose stores hold up every later
+//    LDS wait).
 //  * A few tokens (T <= 16, one token tile): the reduction is split over up to 48 workgroups of
 //    4 wavefronts instead (one workgroup alone would read all the router rows from one CU, at a
 //    small fraction of the chip's rate); their partial logits meet in the workspace, summed in
@@ -47,21 +53,43 @@ __host__ __device__ inline int rt_ksplit(int E) {
   const int n = rt_tiles(E);
   return n >= kRtWaves ? 1 : kRtWaves / n;
 }
-// dynamic LDS: the logits stage's partial tiles, or the bucket's histogram, bases and ids
-// after the tile's logits rows (row reads of the rank may run up to 63 floats past a row) or
-// the bucket's arrays: 512 B of rank keys per wavefront
-__host__ __device__ inline size_t rt_keys_off(size_t rows_bytes, int E, int64_t R) {
-  const size_t p1 = rows_bytes + kWave * sizeof(float);
-  const size_t p2 = (size_t)(2 * E + R) * sizeof(int);
-  return ((p1 > p2 ? p1 : p2) + 15) & ~(size_t)15;
+// The last workgroup's CSR over many tokens: per-group histograms of the picks (a group = one
+// workgroup's 16 tokens), two experts per 32-bit word, when they fit this many bytes of LDS;
+// otherwise every expert sweeps all ids.
+constexpr int kGrpTableBytes = 64 * 1024;
+constexpr int kGrpMaxSeg = 32;   // segments of the prefix over groups
+__host__ __device__ inline int rt_groups(int64_t T) { return (int)((T + kRtTok - 1) / kRtTok); }
+__host__ __device__ inline bool rt_grouped(int G, int E) {
+  return G > 1 && (int64_t)G * ((E + 1) / 2) * 4 <= kGrpTableBytes;
 }
-__host__ inline size_t rt_lds_bytes(int E, int64_t R) {
-  return rt_keys_off((size_t)rt_ksplit(E) * kRtTok * E * sizeof(float), E, R) +
+// LDS of the CSR stage: the group table, expert counts and bases and the segment totals; or the
+// counts, bases and every id
+__host__ __device__ inline size_t rt_csr_bytes(int E, int64_t T, int k) {
+  const int G = rt_groups(T);
+  if (rt_grouped(G, E)) return ((size_t)G * ((E + 1) / 2) + 2 * E + kRtThreads) * sizeof(int);
+  return (size_t)(2 * E + T * k) * sizeof(int);
+}
+// dynamic LDS: the logits stage's partial tiles or the CSR stage's arrays (row reads of the rank
+// may run up to 63 floats past a row), then 512 B of rank keys per wavefront
+__host__ __device__ inline size_t rt_keys_off(size_t rows_bytes, size_t csr_bytes) {
+  const size_t p1 = rows_bytes + kWave * sizeof(float);
+  return ((p1 > csr_bytes ? p1 : csr_bytes) + 15) & ~(size_t)15;
+}
+__host__ inline size_t rt_lds_bytes(int E, int64_t T, int k) {
+  return rt_keys_off((size_t)rt_ksplit(E) * kRtTok * E * sizeof(float), rt_csr_bytes(E, T, k)) +
          (size_t)kRtWaves * kWave * sizeof(uint64_t);
 }
-// split kernel: the tile's logits rows, or the bucket's arrays; then the keys
-__host__ inline size_t sp_lds_bytes(int E, int64_t R) {
-  return rt_keys_off((size_t)kRtTok * E * sizeof(float), E, R) +
+// an upper bound of rt_lds_bytes over every accepted shape
+__host__ inline size_t rt_lds_most() {
+  const size_t rows = (size_t)kRtTok * MOE_MAX_E * sizeof(float);   // ksplit*E <= max(256, E)
+  const size_t grouped = kGrpTableBytes + (2 * MOE_MAX_E + kRtThreads) * sizeof(int);
+  const size_t sweep = (2 * MOE_MAX_E + MOE_ROUTER_MAX_ROUTED) * sizeof(int);
+  return rt_keys_off(rows, grouped > sweep ? grouped : sweep) +
+         (size_t)kRtWaves * kWave * sizeof(uint64_t);
+}
+// split kernel: the tile's logits rows, or the CSR stage's arrays; then the keys
+__host__ inline size_t sp_lds_bytes(int E, int64_t T, int k) {
+  return rt_keys_off((size_t)kRtTok * E * sizeof(float), (size_t)(2 * E + T * k) * sizeof(int)) +
          (size_t)kSpWaves * kWave * sizeof(uint64_t);
 }
 
@@ -99,18 +127,75 @@ __device__ __forceinline__ f32x4_t router_tile(__amdgpu_buffer_rsrc_t rw, __amdg
   return acc0 + acc1;
 }
 
+// Exclusive scan of the padded counts cnt[0..E) into base[] and basep[], counts[] = cnt (E <=
+// the workgroup's threads); returns the padded total. Ends with a barrier.
+__device__ __forceinline__ int csr_bases(const int* cnt, int* base, int E, int tile_m,
+                                         int32_t* __restrict__ counts, int32_t* __restrict__ basep,
+                                         int* wave_tot) {
+  const int tid = (int)threadIdx.x, nthreads = (int)blockDim.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), waves = nthreads >> 6;
+  const int c = tid < E ? cnt[tid] : 0;
+  const int padded = (c + tile_m - 1) / tile_m * tile_m;
+  int incl = padded;
+  for (int m = 1; m < 64; m <<= 1) {
+    const int o = __shfl_up(incl, m);
+    if (lane >= m) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int v = 0; v < waves; ++v) {
+    if (v < wave) before += wave_tot[v];
+    total += wave_tot[v];
+  }
+  const int excl = before + incl - padded;
+  if (tid < E) {
+    base[tid] = excl;
+    counts[tid] = c;
+    basep[tid] = excl;
+  }
+  if (tid == 0) basep[E] = total;
+  __syncthreads();
+  return total;
+}
+
+// Padding rows of every expert (wavefront per expert), then the ghost rows up to mpad_max.
+__device__ __forceinline__ void csr_pad(const int* cnt, const int* base, int E, int tile_m,
+                                        int total, int mpad_max, int32_t* __restrict__ row_tok) {
+  const int tid = (int)threadIdx.x, nthreads = (int)blockDim.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), waves = nthreads >> 6;
+  for (int e = wave; e < E; e += waves) {
+    const int c = cnt[e], b = base[e];
+    const int pe = (c + tile_m - 1) / tile_m * tile_m;
+    for (int j = c + lane; j < pe; j += 64) row_tok[b + j] = -1;
+  }
+  for (int r = total + tid; r < mpad_max; r += nthreads) row_tok[r] = -1;
+}
+
 // The routing of tokens t0.. (at most 16) from their logits rows in LDS (part[tok][E]), then the
 // CSR by the workgroup that holds the last picks. counter: the caller's completion word when
 // several workgroups route (the one that completes the count builds the CSR from the ids in
 // memory), or NULL when this workgroup routes every token (the ids are in its LDS).
 // keys: 512 B of LDS per wavefront for the rank of an E <= 64 row (else unused).
-__device__ void router_tail(float* part, int T, int t0, int E, int k, int tile_m, int mpad_max,
-                            int32_t* __restrict__ ids, float* __restrict__ w,
-                            int32_t* __restrict__ counts, int32_t* __restrict__ basep,
-                            int32_t* __restrict__ row_tok, int32_t* __restrict__ pos,
-                            uint32_t* counter, int n_groups, uint8_t* smem, uint64_t* keys) {
+//
+// The CSR row of pick (t, s) routed to expert e is base[e] plus the number of earlier tokens
+// routed to e (a token picks an expert at most once). With several workgroups (groups of 16
+// tokens) that number splits into the picks of e in earlier groups plus those of earlier tokens
+// of the same group: each workgroup counts the latter for its own picks and leaves them in pos[]
+// (device-scope stores, like the ids); the last workgroup histograms the picks per group in
+// LDS, scans the histograms over the groups, and places every pick at once. When the group
+// table does not fit, each wavefront of the last workgroup sweeps all ids for its experts.
+__device__ __forceinline__ void router_tail(float* part, int T, int t0, int E, int k, int tile_m,
+                                            int mpad_max, int32_t* __restrict__ ids,
+                                            float* __restrict__ w, int32_t* __restrict__ counts,
+                                            int32_t* __restrict__ basep,
+                                            int32_t* __restrict__ row_tok,
+                                            int32_t* __restrict__ pos, uint32_t* counter,
+                                            int n_groups, uint8_t* smem, uint64_t* keys) {
   __shared__ int s_last;
-  __shared__ int s_ids[kRtTok * MOE_MAX_K];   // this workgroup's picks
+  __shared__ __attribute__((aligned(16))) int s_ids[kRtTok * MOE_MAX_K];   // this group's picks
   __shared__ int s_wave_tot[kRtWaves];
   const int tid = (int)threadIdx.x, nthreads = (int)blockDim.x;
   const int lane = tid & 63;
@@ -141,81 +226,163 @@ __device__ void router_tail(float* part, int T, int t0, int E, int k, int tile_m
       s_ids[tt * k + lane] = my_id;
     }
   }
-
-  // ---- the last workgroup builds the CSR ----
-  // Every wavefront waits until its stores are acknowledged, then the workgroup counts itself
-  // in; the one that completes the count reads the ids with device-scope atomic loads. (A
-  // device-scope fence would also work but writes back and invalidates the whole L2, which
-  // costs microseconds per workgroup.)
-  const bool alone = counter == nullptr;
-  if (!alone) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __syncthreads();
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               (uint32_t)n_groups - 1;
-    __syncthreads();
-    if (!s_last) return;
-  } else {
-    __syncthreads();
-  }
-
   const int R = T * k;
-  int* hist = reinterpret_cast<int*>(smem);
-  int* base = hist + E;
-  int* idl = base + E;
-  for (int i = tid; i < E; i += nthreads) hist[i] = 0;
+  const bool alone = counter == nullptr;
   __syncthreads();
-  for (int i = tid; i < R; i += nthreads) {
-    const int id = alone ? s_ids[i]
-                         : __hip_atomic_load(ids + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    idl[i] = id;
-    if ((unsigned)id < (unsigned)E) atomicAdd(&hist[id], 1);
-  }
-  __syncthreads();
-  // exclusive scan of the padded counts over the experts (E <= nthreads: one per thread)
-  const int cnt = tid < E ? hist[tid] : 0;
-  const int padded = (cnt + tile_m - 1) / tile_m * tile_m;
-  int incl = padded;
-  for (int m = 1; m < 64; m <<= 1) {
-    const int o = __shfl_up(incl, m);
-    if (lane >= m) incl += o;
-  }
-  if (lane == 63) s_wave_tot[wave] = incl;
-  __syncthreads();
-  int before = 0, total = 0;
-  for (int v = 0; v < waves; ++v) {
-    if (v < wave) before += s_wave_tot[v];
-    total += s_wave_tot[v];
-  }
-  const int excl = before + incl - padded;
-  if (tid < E) {
-    base[tid] = excl;
-    counts[tid] = cnt;
-    basep[tid] = excl;
-  }
-  if (tid == 0) basep[E] = total;
-  __syncthreads();
+
   if (alone) {
-    // every routed row at once: the CSR row of (t, s) follows the earlier tokens routed to the
-    // same expert (a token picks an expert at most once); then each expert's padding rows
+    // every routed row at once, its rank counted over the earlier picks in LDS; then the padding
+    int* cnt = reinterpret_cast<int*>(smem);
+    int* base = cnt + E;
+    for (int i = tid; i < E; i += nthreads) cnt[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < R; i += nthreads)
+      if ((unsigned)s_ids[i] < (unsigned)E) atomicAdd(&cnt[s_ids[i]], 1);
+    __syncthreads();
+    const int total = csr_bases(cnt, base, E, tile_m, counts, basep, s_wave_tot);
     for (int r = tid; r < R; r += nthreads) {
-      const int e = idl[r], t = r / k;
+      const int e = s_ids[r], t = r / k;
       if ((unsigned)e >= (unsigned)E) continue;
       int rank = 0;
-      for (int r2 = 0; r2 < t * k; ++r2) rank += idl[r2] == e;
+      for (int r2 = 0; r2 < t * k; ++r2) rank += s_ids[r2] == e;
       pos[r] = base[e] + rank;
       row_tok[base[e] + rank] = t0 + t;
     }
-    for (int e = tid; e < E; e += nthreads) {
-      const int c = hist[e];
-      const int pe = (c + tile_m - 1) / tile_m * tile_m;
-      for (int j = c; j < pe; ++j) row_tok[base[e] + j] = -1;
-    }
-    for (int r = total + tid; r < mpad_max; r += nthreads) row_tok[r] = -1;   // ghost rows
+    csr_pad(cnt, base, E, tile_m, total, mpad_max, row_tok);
     return;
   }
-  // ordered compaction: wavefront v owns experts v, v + waves, ...
+
+  // ---- several workgroups: this group's in-group ranks, then the last one builds the CSR ----
+  const int G = n_groups;
+  const bool grouped = rt_grouped(G, E);
+  if (grouped) {
+    const int ntok = min(kRtTok, T - t0);
+    for (int i = tid; i < ntok * k; i += nthreads) {
+      const int e = s_ids[i], before = (i / k) * k;
+      int lr = 0, j = 0;
+      for (; j + 4 <= before; j += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(s_ids + j);
+        lr += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+      }
+      for (; j < before; ++j) lr += s_ids[j] == e;
+      __hip_atomic_store(pos + (size_t)t0 * k + i, lr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // Every wavefront waits until its stores are acknowledged, then the workgroup counts itself
+  // in; the one that completes the count reads the ids (and in-group ranks) with device-coherent
+  // loads (sc1, as the device-scope stores that wrote them), all in flight at once. (A
+  // device-scope fence would also work but writes back and invalidates the whole L2, which
+  // costs microseconds per workgroup.)
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)G - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (tid == 0)   // ready for the next call
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  constexpr int kPer = MOE_ROUTER_MAX_ROUTED / kRtThreads;   // picks per thread: r = tid + i*1024
+  const __amdgpu_buffer_rsrc_t rid = make_rsrc(ids, (uint32_t)R * 4);
+  const __amdgpu_buffer_rsrc_t rpos = make_rsrc(pos, (uint32_t)R * 4);
+  int my_e[kPer], my_lr[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    my_e[i] = -1;
+    my_lr[i] = 0;
+    if (i * kRtThreads < R) {   // uniform over the workgroup
+      const int r = tid + i * kRtThreads;
+      const uint32_t off = r < R ? (uint32_t)r * 4 : kOOB;
+      my_e[i] = r < R ? (int)__builtin_amdgcn_raw_buffer_load_b32(rid, off, 0, 16) : -1;
+      if (grouped) my_lr[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rpos, off, 0, 16);
+    }
+  }
+
+  if (grouped) {
+    // LDS: tbl[G][EW] (experts 2w and 2w+1 in the low and high halves of word w), cnt[E],
+    // base[E], seg[S][EW]
+    const int EW = (E + 1) >> 1;
+    uint32_t* tbl = reinterpret_cast<uint32_t*>(smem);
+    int* cnt = reinterpret_cast<int*>(tbl + (size_t)G * EW);
+    int* base = cnt + E;
+    uint32_t* seg = reinterpret_cast<uint32_t*>(base + E);
+    for (int i = tid; i < G * EW; i += nthreads) tbl[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = my_e[i];
+      if ((unsigned)e < (unsigned)E) {
+        const int g = ((tid + i * kRtThreads) / k) / kRtTok;
+        atomicAdd(&tbl[g * EW + (e >> 1)], (e & 1) ? 0x10000u : 1u);
+      }
+    }
+    __syncthreads();
+    // exclusive prefix of each column over the groups: S segments of L groups each (a half-word
+    // never exceeds T <= MOE_ROUTER_MAX_ROUTED, so the halves do not carry into each other)
+    const int S = min(min(nthreads / EW, kGrpMaxSeg), G);
+    const int L = (G + S - 1) / S;
+    const int col = tid % EW, sg = tid / EW;
+    const int g0 = sg * L, g1 = min(G, g0 + L);
+    if (sg < S) {
+      uint32_t sum = 0;
+      for (int g = g0; g < g1; ++g) sum += tbl[g * EW + col];
+      seg[sg * EW + col] = sum;
+    }
+    __syncthreads();
+    if (tid < EW) {
+      uint32_t run = 0;
+      for (int q = 0; q < S; ++q) {
+        const uint32_t v = seg[q * EW + tid];
+        seg[q * EW + tid] = run;
+        run += v;
+      }
+      cnt[2 * tid] = (int)(run & 0xFFFFu);
+      if (2 * tid + 1 < E) cnt[2 * tid + 1] = (int)(run >> 16);
+    }
+    __syncthreads();
+    if (sg < S) {
+      uint32_t run = seg[sg * EW + col];
+      for (int g = g0; g < g1; ++g) {
+        const uint32_t v = tbl[g * EW + col];
+        tbl[g * EW + col] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    const int total = csr_bases(cnt, base, E, tile_m, counts, basep, s_wave_tot);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = my_e[i];
+      if ((unsigned)e < (unsigned)E) {
+        const int r = tid + i * kRtThreads, t = r / k;
+        const uint32_t word = tbl[(t / kRtTok) * EW + (e >> 1)];
+        const int row = base[e] + (int)((word >> ((e & 1) * 16)) & 0xFFFFu) + my_lr[i];
+        pos[r] = row;
+        row_tok[row] = t;
+      }
+    }
+    csr_pad(cnt, base, E, tile_m, total, mpad_max, row_tok);
+    return;
+  }
+
+  // the group table does not fit: every id into LDS, then wavefront v owns experts v, v +
+  // waves, ... and sweeps all tokens in ascending order, one ballot per 64 tokens
+  int* cnt = reinterpret_cast<int*>(smem);
+  int* base = cnt + E;
+  int* idl = base + E;
+  for (int i = tid; i < E; i += nthreads) cnt[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int r = tid + i * kRtThreads, e = my_e[i];
+    if (r < R) {
+      idl[r] = e;
+      if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  const int total = csr_bases(cnt, base, E, tile_m, counts, basep, s_wave_tot);
   for (int e = wave; e < E; e += waves) {
     const int b = base[e];
     int running = 0;
@@ -233,12 +400,8 @@ __device__ void router_tail(float* part, int T, int t0, int E, int k, int tile_m
       }
       running += __popcll(ballot);
     }
-    const int pe = (running + tile_m - 1) / tile_m * tile_m;
-    for (int r = b + running + lane; r < b + pe; r += 64) row_tok[r] = -1;   // padding rows
   }
-  for (int r = total + tid; r < mpad_max; r += nthreads) row_tok[r] = -1;   // ghost rows
-  if (tid == 0 && !alone)   // ready for the next call
-    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  csr_pad(cnt, base, E, tile_m, total, mpad_max, row_tok);
 }
 
 // Workgroups of 16 wavefronts each take 16 tokens over the whole reduction.
@@ -283,7 +446,7 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
   }
   __syncthreads();
   uint64_t* const keys = reinterpret_cast<uint64_t*>(
-      smem + rt_keys_off((size_t)ksplit * kRtTok * E * sizeof(float), E, (int64_t)T * k));
+      smem + rt_keys_off((size_t)ksplit * kRtTok * E * sizeof(float), rt_csr_bytes(E, T, k)));
   router_tail(part, T, t0, E, k, tile_m, mpad_max, ids, w, counts, basep, row_tok, pos,
               gridDim.x == 1 ? nullptr : ws, (int)gridDim.x, smem, keys);
 }
@@ -356,7 +519,7 @@ router_split_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
   if (tid == 0) __hip_atomic_store(ws, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   uint64_t* const keys = reinterpret_cast<uint64_t*>(
-      smem + rt_keys_off((size_t)kRtTok * E * sizeof(float), E, (int64_t)T * k));
+      smem + rt_keys_off((size_t)kRtTok * E * sizeof(float), (size_t)(2 * E + T * k) * sizeof(int)));
   router_tail(part, T, 0, E, k, tile_m, mpad_max, ids, w, counts, basep, row_tok, pos, nullptr,
               1, smem, keys);
 }
@@ -387,16 +550,16 @@ extern "C" int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b
   }
   if (nsplit >= 2) {
     moe::launch(moe::router_split_kernel, dim3((unsigned)nsplit), dim3(moe::kSpThreads),
-                (unsigned)moe::sp_lds_bytes(E, T * k), (hipStream_t)stream, x, w_r, b_r, (int)T, D,
+                (unsigned)moe::sp_lds_bytes(E, T, k), (hipStream_t)stream, x, w_r, b_r, (int)T, D,
                 E, k, tile_m, (int)mpad_max, logits, ids, w, counts, basep, row_tok, pos, ws,
                 nsplit);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
   }
-  const size_t lds = moe::rt_lds_bytes(E, T * k);
+  const size_t lds = moe::rt_lds_bytes(E, T, k);
   static bool lds_attr_set[moe::kMaxDevices] = {};   // > 64 KB of LDS: opt in once per device
   const int dslot = moe::device_slot();
   if (dslot < 0 || !lds_attr_set[dslot]) {
-    const size_t most = moe::rt_lds_bytes(MOE_MAX_E, MOE_ROUTER_MAX_ROUTED);
+    const size_t most = moe::rt_lds_most();
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::router_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)most) != hipSuccess)
       return MOE_ELAUNCH;

@@ -5,7 +5,9 @@ Protocol: the fp32 logits within |gpu - ref| <= 1e-3 * S + 1e-5 of oracle.router
 routing decisions taken on the GPU's own fp32 logits (ids, weights) and the CSR built from the
 GPU's ids equal the oracle's route_topk and bucket bit for bit; the workspace's counter word is
 left zero. A few tokens (T <= 16, E <= 256) take the split-reduction kernel, more the
-one-workgroup-per-16-tokens kernel; both are covered, and one workspace serves both in turn.
+one-workgroup-per-16-tokens kernel, whose last workgroup builds the CSR from per-group
+histograms (or, when their table does not fit its LDS, by sweeping all ids per expert); each is
+covered, and one workspace serves both kernels in turn.
 """
 import numpy as np
 import pytest
@@ -81,6 +83,12 @@ CASES = {
     "one_expert": dict(T=20, D=32, E=1, k=1, tile_m=4),
     "E_not_tile": dict(T=19, D=64, E=21, k=3, tile_m=5),
     "max_routed": dict(T=4096, D=64, E=64, k=4, tile_m=8),
+    # in-group ranks over 16 picks per token, T*k at the limit
+    "k16_max_routed": dict(T=1024, D=32, E=64, k=16, tile_m=4),
+    # odd E on the grouped path: the last table word holds one expert
+    "grouped_E255": dict(T=40, D=64, E=255, k=5, tile_m=3),
+    # per-group table past its LDS budget: every expert sweeps all ids
+    "sweep_E1024": dict(T=600, D=32, E=1024, k=4, tile_m=3),
 }
 
 
