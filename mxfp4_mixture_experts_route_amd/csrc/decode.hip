@@ -130,11 +130,9 @@ __device__ __forceinline__ void gate_up_item(const float* __restrict__ logits,
       // lrow: 0 past E (read past the resource)
       e0 = rank_pick(wave_rank_lds(lrow, reinterpret_cast<uint64_t*>(slot0 + 256), E), slot);
     } else {
-      float lv[kRoutePerLane];
-      wave_topk_load(logits + (size_t)t * E, E, lv);
       int my_id;
       float my_v;
-      wave_topk_select(lv, E, k, my_id, my_v);
+      wave_topk(logits + (size_t)t * E, E, k, my_id, my_v);
       e0 = __shfl(my_id, slot);
     }
     if (lane == 0) *pick = e0;

@@ -45,12 +45,14 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Logits of one row for wave_topk_select: lane l holds experts j*64 + l (0 past E).
+// Logits of one row for wave_topk_select: lane l holds experts j*64 + l (0 past E); N values per
+// lane cover E <= 64 N.
+template <int N = kRoutePerLane>
 __device__ __forceinline__ void wave_topk_load(const float* __restrict__ row, int E,
-                                               float (&v)[kRoutePerLane]) {
+                                               float (&v)[N]) {
   const int lane = (int)(threadIdx.x & 63);
 #pragma unroll
-  for (int j = 0; j < kRoutePerLane; ++j) {
+  for (int j = 0; j < N; ++j) {
     const int e = j * kWave + lane;
     v[j] = (e < E) ? row[e] : 0.0f;
   }
@@ -59,12 +61,13 @@ __device__ __forceinline__ void wave_topk_load(const float* __restrict__ row, in
 // The k best experts of one logits row (E <= MOE_MAX_E, k <= min(E, MOE_MAX_K)) held as by
 // wave_topk_load. Lane r < k ends with the r-th pick in (my_id, my_v); other lanes' outputs are
 // unspecified. k rounds of a wavefront arg-max over the lanes' best remaining keys; no LDS.
-__device__ __forceinline__ void wave_topk_select(const float (&v)[kRoutePerLane], int E, int k,
+template <int N = kRoutePerLane>
+__device__ __forceinline__ void wave_topk_select(const float (&v)[N], int E, int k,
                                                  int& my_id, float& my_v) {
   const int lane = (int)(threadIdx.x & 63);
-  uint64_t key[kRoutePerLane];   // 0: absent or already chosen
+  uint64_t key[N];   // 0: absent or already chosen
 #pragma unroll
-  for (int j = 0; j < kRoutePerLane; ++j) {
+  for (int j = 0; j < N; ++j) {
     const int e = j * kWave + lane;
     key[j] = e < E ? rank_key(v[j], e) : 0u;
   }
@@ -73,7 +76,7 @@ __device__ __forceinline__ void wave_topk_select(const float (&v)[kRoutePerLane]
   for (int r = 0; r < k; ++r) {
     uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < kRoutePerLane; ++j) best = key[j] > best ? key[j] : best;
+    for (int j = 0; j < N; ++j) best = key[j] > best ? key[j] : best;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
       const uint64_t o = shfl_xor_u64(best, m);
@@ -83,7 +86,7 @@ __device__ __forceinline__ void wave_topk_select(const float (&v)[kRoutePerLane]
     const int jw = id >> 6, lw = id & 63;
     float cand = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kRoutePerLane; ++j) {
+    for (int j = 0; j < N; ++j) {
       if (j == jw) {
         cand = v[j];
         if (lane == lw) key[j] = 0u;
@@ -159,9 +162,20 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
     }
     return;
   }
-  float v[kRoutePerLane];
-  wave_topk_load(row, E, v);
-  wave_topk_select(v, E, k, my_id, my_v);
+  // as few values per lane as E needs: the arg-max rounds scan every one of them
+  if (E <= 2 * kWave) {
+    float v[2];
+    wave_topk_load(row, E, v);
+    wave_topk_select(v, E, k, my_id, my_v);
+  } else if (E <= 4 * kWave) {
+    float v[4];
+    wave_topk_load(row, E, v);
+    wave_topk_select(v, E, k, my_id, my_v);
+  } else {
+    float v[kRoutePerLane];
+    wave_topk_load(row, E, v);
+    wave_topk_select(v, E, k, my_id, my_v);
+  }
 }
 
 // Routing weight of the pick held by this lane (lanes 0..k-1 of wave_topk): the softmax over the

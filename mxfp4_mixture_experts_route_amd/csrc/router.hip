@@ -9,10 +9,11 @@
 //
 // gfx950 mapping. Workgroups of 16 wavefronts each take 16 tokens:
 //  * logits: v_mfma_f32_16x16x32_bf16 with 16 router rows (experts) as the A operand and the 16
-//    tokens as the B columns; the K = D reduction is split over the wavefronts that share an
-//    expert tile (16 / ceil(E/16) of them), whose partial tiles meet in LDS and are summed in a
-//    fixed order, then the bias is added. Loads are buffer loads: tokens past T and experts past
-//    E read zeros.
+//    tokens as the B columns. A wavefront holds up to 4 expert tiles, which share each load of
+//    the tokens' operand; the K = D reduction is split over the wavefronts that hold the same
+//    tiles (16 / ceil(E/64) of them), whose partial tiles meet in LDS and are summed in a fixed
+//    order, then the bias is added. Loads are buffer loads: tokens past T and experts past E
+//    read zeros.
 //  * top-k: one wavefront per token on the LDS logits row (the moe_route_topk code).
 //  * bucket: the CSR needs every token's ids, so the LAST workgroup to finish its tokens builds
 //    it: each workgroup stores its ids, and for each pick the number of earlier picks of the
@@ -47,10 +48,14 @@ constexpr int kSpThreads = kSpWaves * kWave;
 constexpr int kSpMaxSplit = 48;
 constexpr int kRtPartOff = 64;   // workspace words before the split kernel's partial logits
 
-// expert tiles and the K split of the logits stage
+constexpr int kRtTpw = 4;    // expert tiles per wavefront in the logits stage of router_kernel
+
+// expert tiles, their groups of kRtTpw and the K split of the logits stage (a wavefront per
+// tile group and K slice)
 __host__ __device__ inline int rt_tiles(int E) { return (E + 15) / 16; }
+__host__ __device__ inline int rt_tgroups(int E) { return (rt_tiles(E) + kRtTpw - 1) / kRtTpw; }
 __host__ __device__ inline int rt_ksplit(int E) {
-  const int n = rt_tiles(E);
+  const int n = rt_tgroups(E);
   return n >= kRtWaves ? 1 : kRtWaves / n;
 }
 // The last workgroup's CSR over many tokens: per-group histograms of the picks (a group = one
@@ -81,7 +86,7 @@ __host__ inline size_t rt_lds_bytes(int E, int64_t T, int k) {
 }
 // an upper bound of rt_lds_bytes over every accepted shape
 __host__ inline size_t rt_lds_most() {
-  const size_t rows = (size_t)kRtTok * MOE_MAX_E * sizeof(float);   // ksplit*E <= max(256, E)
+  const size_t rows = (size_t)kRtTok * MOE_MAX_E * sizeof(float);   // ksplit*E <= 1024
   const size_t grouped = kGrpTableBytes + (2 * MOE_MAX_E + kRtThreads) * sizeof(int);
   const size_t sweep = (2 * MOE_MAX_E + MOE_ROUTER_MAX_ROUTED) * sizeof(int);
   return rt_keys_off(rows, grouped > sweep ? grouped : sweep) +
@@ -404,6 +409,48 @@ __device__ __forceinline__ void router_tail(float* part, int T, int t0, int E, i
   csr_pad(cnt, base, E, tile_m, total, mpad_max, row_tok);
 }
 
+// nt <= kRtTpw logits tiles of 16 experts each (from e_row0, 16 apart) and the 16 tokens from
+// t0, over k steps [s0, s1) of 32, as router_tile; the tokens' operand is loaded once per step
+// and shared by the tiles (the wavefront's share of the workgroup's reads of x falls with the
+// number of tiles it holds). 4 steps per round, all loads of a round in flight before its
+// MFMAs, which alternate between the tiles' accumulators.
+__device__ __forceinline__ void router_tiles(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx,
+                                             int D, int E, int T, int e_row0, int nt, int t0,
+                                             int s0, int s1, f32x4_t (&acc)[kRtTpw]) {
+  const int lane = (int)(threadIdx.x & 63), lr = lane & 15, lg = lane >> 4;
+  uint32_t ao[kRtTpw];
+#pragma unroll
+  for (int j = 0; j < kRtTpw; ++j) {
+    const int e_row = e_row0 + 16 * j + lr;
+    ao[j] = j < nt && e_row < E ? ((uint32_t)e_row * D + 8 * lg) * 2 : kOOB;
+    acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const uint32_t bo = t0 + lr < T ? ((uint32_t)(t0 + lr) * D + 8 * lg) * 2 : kOOB;
+  for (int sb = s0; sb < s1; sb += 4) {
+    u32x4_t a[kRtTpw][4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = sb + i < s1;
+      b[i] = buf_load16(rx, ok ? bo : kOOB, (uint32_t)(sb + i) * 64);
+#pragma unroll
+      for (int j = 0; j < kRtTpw; ++j)
+        if (j < nt) a[j][i] = buf_load16(rw, ok ? ao[j] : kOOB, (uint32_t)(sb + i) * 64);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x8_t B;
+      __builtin_memcpy(&B, &b[i], 16);
+#pragma unroll
+      for (int j = 0; j < kRtTpw; ++j)
+        if (j < nt) {
+          bf16x8_t A;
+          __builtin_memcpy(&A, &a[j][i], 16);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[j], 0, 0, 0);
+        }
+    }
+  }
+}
+
 // Workgroups of 16 wavefronts each take 16 tokens over the whole reduction.
 __global__ void __launch_bounds__(kRtThreads)
 router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
@@ -418,22 +465,26 @@ router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const int t0 = (int)blockIdx.x * kRtTok;
-  const int ntiles = rt_tiles(E), ksplit = rt_ksplit(E);
+  const int ntiles = rt_tiles(E), ntg = rt_tgroups(E), ksplit = rt_ksplit(E);
   const int KS = D >> 5;   // 32-wide k steps
   float* part = reinterpret_cast<float*>(smem);   // [ksplit][kRtTok][E]
 
-  // ---- logits of the workgroup's 16 tokens ----
+  // ---- logits of the workgroup's 16 tokens: a wavefront per (tile group, K slice) ----
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wr, (uint32_t)E * D * 2);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)T * D * 2);
-  for (int u = wave; u < ntiles * ksplit; u += kRtWaves) {
-    const int tile = u % ntiles, p = u / ntiles;
-    const f32x4_t acc = router_tile(rw, rx, D, E, T, tile * 16, t0, p * KS / ksplit,
-                                    (p + 1) * KS / ksplit);
+  for (int u = wave; u < ntg * ksplit; u += kRtWaves) {
+    const int tg = u % ntg, p = u / ntg;
+    const int nt = min(kRtTpw, ntiles - tg * kRtTpw);
+    f32x4_t acc[kRtTpw];
+    router_tiles(rw, rx, D, E, T, tg * kRtTpw * 16, nt, t0, p * KS / ksplit,
+                 (p + 1) * KS / ksplit, acc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tile * 16 + 4 * lg + i;
-      if (e < E) part[((size_t)p * kRtTok + lr) * E + e] = acc[i];
-    }
+    for (int j = 0; j < kRtTpw; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = (tg * kRtTpw + j) * 16 + 4 * lg + i;
+        if (j < nt && e < E) part[((size_t)p * kRtTok + lr) * E + e] = acc[j][i];
+      }
   }
   __syncthreads();
   for (int i = tid; i < kRtTok * E; i += kRtThreads) {
