@@ -86,10 +86,16 @@ typedef enum {
 #define MOE_GEMV_MAX_K 16384 /* reduction length of mx4_moe_gemv (mx4_moe_gemm has no limit) */
 #define MOE_SCALE_ROW_ALIGN 16 /* bytes: scale rows of the chunked layout are padded to this */
 
-/* Static, NUL-terminated description of a status code (never NULL). */
+/* Host helper of the boundary (no passage: the pages define no error reporting). Static,
+   NUL-terminated description of a status code (never NULL); unknown codes get a generic text. */
 const char* moe_strerror(int status);
 
 /*
+ * Host helper (no kernel). Follows PR #3579 "dasLLAMA gpt-oss arc", Metal fusion-lane commit:
+ * the bucket pads every expert's run of rows to the matmul's tile granule and places the runs at
+ * padded prefix bases, so the row space the CSR needs is bounded as below (the pages give no
+ * formula; this is the plain bound of that layout, and the caller sizes row_tok and the GEMM
+ * outputs with it).
  * Row capacity of the CSR for T tokens routed to k of E experts with padding granule tile_m:
  *   R = T*k routed rows; every non-empty expert pads its rows up to a multiple of tile_m, so at
  *   most min(E, R) experts each add at most tile_m-1 padding rows:

@@ -144,6 +144,9 @@ __device__ __forceinline__ int rank_pick(int rank, int slot) {
   return __ffsll((unsigned long long)__ballot(rank == slot)) - 1;
 }
 
+// The k best experts of one logits row in memory (E <= MOE_MAX_E, k <= min(E, MOE_MAX_K)), by
+// the total order of rank_key: lane r < k ends with the r-th pick in (my_id, my_v). E <= 64:
+// one rank pass (wave_rank_row); more: k arg-max rounds over as few values per lane as E needs.
 __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int& my_id,
                                           float& my_v) {
   if (E <= kWave) {
