@@ -226,7 +226,7 @@ int mx4_moe_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const 
                  int act, float alpha, float limit, void* out, void* stream);
 
 #define MOE_ROUTER_MAX_ROUTED 16384  /* T*k of one moe_router call */
-#define MOE_ROUTER_WS_WORDS 16448    /* u32 workspace words of moe_router */
+#define MOE_ROUTER_WS_WORDS 67584    /* u32 workspace words of moe_router */
 
 /*
  * The router projection and the routing front of the chain in one launch: the step before the
@@ -239,15 +239,17 @@ int mx4_moe_gemm(const uint16_t* a, const int32_t* a_row, int64_t a_rows, const 
  *   x     bf16 [T][D];  w_r bf16 [E][D];  b_r f32 [E] or NULL.
  *   logits f32 [T][E] out, or NULL (then not written).
  *   ws    u32 [MOE_ROUTER_WS_WORDS] device workspace owned by the caller: zero before the first
- *         call, then left to the library (every call leaves word 0, its completion counter,
- *         zero; the rest holds the last call's partial logits). The workgroup that finishes last
- *         builds the CSR, found by counting on word 0, so calls that can run concurrently need
- *         distinct workspaces.
- * For T <= 16 and E <= 256 the reduction over D is split over up to 48 workgroups, whose
- * partial logits are summed in a fixed order (results are deterministic; they differ from the
- * one-workgroup sum only by fp32 association). Cost: the CSR is built by one workgroup, in time
- * proportional to E * T / 64 steps per wavefront; for large E * T the separate moe_route_topk +
- * moe_bucket (one workgroup per expert) spread that work wider.
+ *         call, then left to the library. Word 0 and words 64..1087 are completion counters
+ *         that every call leaves zero; the rest holds the last call's partial logits or top-k
+ *         candidates. Calls that can run concurrently need distinct workspaces.
+ * Work split: for T <= 16 and E <= 256 the reduction over D is split over up to 48 workgroups,
+ * whose partial logits are summed in a fixed order (results are deterministic; they differ from
+ * the one-workgroup sum only by fp32 association). Otherwise a workgroup takes 16 tokens; for
+ * E >= 64 and at most one round of pairs over the CUs, a pair of workgroups takes them, each
+ * with half of the experts, and the later of the pair merges the two halves' top-k candidates
+ * (the same picks as one pass). The workgroup that finishes last builds the CSR (from
+ * per-group histograms that fit 64 KB of LDS, else by sweeping all ids per expert), found by
+ * counting on word 0; no workgroup waits for another.
  * Errors: MOE_EINVAL for NULL pointers (other than b_r, logits), T, D or E < 1, k < 1,
  *         k > min(E, MOE_MAX_K); MOE_ESHAPE for D % 32 != 0, T*k > MOE_ROUTER_MAX_ROUTED,
  *         E > MOE_MAX_E, tile_m outside [1, MOE_MAX_TILE_M], mpad_max < moe_mpad_max(T, k, E,

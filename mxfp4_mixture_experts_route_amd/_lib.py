@@ -24,7 +24,7 @@ EXPORTS = ("moe_strerror", "moe_mpad_max", "moe_route_topk", "moe_bucket", "mx4_
            "moe_probe_mfma_bf16")
 MOE_DECODE_WS_WORDS = 544
 MOE_ROUTER_MAX_ROUTED = 16384
-MOE_ROUTER_WS_WORDS = 16448
+MOE_ROUTER_WS_WORDS = 67584
 MOE_MX8_GEMM_MAX_K = 4096
 
 

@@ -100,17 +100,16 @@ __device__ __forceinline__ void wave_topk_select(const float (&v)[N], int E, int
   }
 }
 
-// E <= 64: the rank of every lane's logit among the row's E logits (the number that rank before
-// it), the lane of rank r holding pick r; E or more for lanes >= E. From the logits row staged in
-// LDS (row[0..63]; what lies past E is never compared) and 64 keys of LDS scratch of the calling
-// wavefront: every lane writes its key, then reads all of them eight at a time (broadcast reads;
-// the LDS operations of a wavefront complete in order) and counts the larger ones.
-__device__ __forceinline__ int wave_rank_lds(const float* row, uint64_t* keys, int E) {
+// The rank of every lane's key among the keys of lanes 0..n-1 (n <= 64; the number of larger
+// ones), n or more for lanes >= n. Keys of real entries are nonzero (rank_key's low word is the
+// complemented id). Every lane writes its key into the wavefront's 64 keys of LDS scratch, then
+// reads all of them eight at a time (broadcast reads; the LDS operations of a wavefront complete
+// in order) and counts the larger ones.
+__device__ __forceinline__ int wave_rank_keys(uint64_t mk, uint64_t* keys, int n) {
   const int lane = (int)(threadIdx.x & 63);
-  const uint64_t mk = rank_key(row[lane], lane);
-  keys[lane] = lane < E ? mk : 0u;
+  keys[lane] = lane < n ? mk : 0u;
   int rank = 0;
-  for (int j0 = 0; j0 < E; j0 += 8) {   // j0 + 8 <= 64; keys past E are 0 and never count
+  for (int j0 = 0; j0 < n; j0 += 8) {   // j0 + 8 <= 64; keys past n are 0 and never count
     const ulonglong2 a0 = *reinterpret_cast<const ulonglong2*>(keys + j0);
     const ulonglong2 a1 = *reinterpret_cast<const ulonglong2*>(keys + j0 + 2);
     const ulonglong2 a2 = *reinterpret_cast<const ulonglong2*>(keys + j0 + 4);
@@ -118,7 +117,16 @@ __device__ __forceinline__ int wave_rank_lds(const float* row, uint64_t* keys, i
     rank += (a0.x > mk) + (a0.y > mk) + (a1.x > mk) + (a1.y > mk) + (a2.x > mk) +
             (a2.y > mk) + (a3.x > mk) + (a3.y > mk);
   }
-  return lane < E ? rank : E + lane;
+  return lane < n ? rank : n + lane;
+}
+
+// E <= 64: the rank of every lane's logit among the row's E logits (the number that rank before
+// it), the lane of rank r holding pick r; E or more for lanes >= E. From the logits row staged in
+// LDS (row[0..63]; what lies past E is never compared) and 64 keys of LDS scratch of the calling
+// wavefront.
+__device__ __forceinline__ int wave_rank_lds(const float* row, uint64_t* keys, int E) {
+  const int lane = (int)(threadIdx.x & 63);
+  return wave_rank_keys(rank_key(row[lane], lane), keys, E);
 }
 
 // The same ranks from a logits row in memory (E <= 64): eight values per step by loads every

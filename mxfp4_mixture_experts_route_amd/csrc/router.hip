@@ -28,6 +28,11 @@
 //    tail is inlined into each kernel so that its LDS and global accesses keep their address
 //    spaces (as a called function they become flat accesses, whose stores hold up every later
 //    LDS wait).
+//  * E >= 64 (and the pairs' grid within one round over the CUs): each 16-token group is routed
+//    by a pair of workgroups with half of the experts each, so each streams half of W_r; each
+//    takes the top k of its half, stores those candidates in the workspace and counts itself in
+//    on its group's word; the later of the pair merges both halves' candidates under the same
+//    order (the top k of the union of the halves' top k is the row's top k) and goes on as one.
 //  * A few tokens (T <= 16, one token tile): the reduction is split over up to 48 workgroups of
 //    4 wavefronts instead (one workgroup alone would read all the router rows from one CU, at a
 //    small fraction of the chip's rate); their partial logits meet in the workspace, summed in
@@ -46,13 +51,29 @@ constexpr int kRtTok = 16;   // tokens per workgroup
 constexpr int kSpWaves = 4;  // split kernel: wavefronts per workgroup
 constexpr int kSpThreads = kSpWaves * kWave;
 constexpr int kSpMaxSplit = 48;
-constexpr int kRtPartOff = 64;   // workspace words before the split kernel's partial logits
+// workspace words: [0] the completion counter; [kRtGrpOff, +kRtMaxGroups) the expert-split
+// pairs' counters (zero between calls); from kRtDataOff, the split kernel's partial logits or
+// the expert-split halves' candidates
+constexpr int kRtGrpOff = 64;
+constexpr int kRtMaxGroups = MOE_ROUTER_MAX_ROUTED / 16;
+constexpr int kRtDataOff = kRtGrpOff + kRtMaxGroups;
+constexpr int kRtParts = 2;   // expert split of the many-token kernel
+static_assert(kRtDataOff + kRtParts * 2 * (MOE_ROUTER_MAX_ROUTED + 15 * MOE_MAX_K) <=
+                  MOE_ROUTER_WS_WORDS, "router workspace");
 
 constexpr int kRtTpw = 4;    // expert tiles per wavefront in the logits stage of router_kernel
 
 // expert tiles, their groups of kRtTpw and the K split of the logits stage (a wavefront per
 // tile group and K slice)
 __host__ __device__ inline int rt_tiles(int E) { return (E + 15) / 16; }
+// Parts of the expert split: with several workgroups (T > 16), E >= 64 (W_r large enough that
+// streaming half of it pays for the merge) and the pairs' grid within one round over the CUs,
+// each 16-token group is routed by a pair of workgroups holding half of the experts each (so
+// each streams half of W_r), whose top-k candidates the later one of the pair merges.
+__host__ inline int rt_parts(int64_t T, int E, int cus) {
+  return (T > kRtTok && E >= 64 && (T + kRtTok - 1) / kRtTok * kRtParts <= cus) ? kRtParts : 1;
+}
+__host__ __device__ inline int rt_part_experts(int E, int P) { return (E + P - 1) / P; }
 __host__ __device__ inline int rt_tgroups(int E) { return (rt_tiles(E) + kRtTpw - 1) / kRtTpw; }
 __host__ __device__ inline int rt_ksplit(int E) {
   const int n = rt_tgroups(E);
@@ -80,8 +101,9 @@ __host__ __device__ inline size_t rt_keys_off(size_t rows_bytes, size_t csr_byte
   const size_t p1 = rows_bytes + kWave * sizeof(float);
   return ((p1 > csr_bytes ? p1 : csr_bytes) + 15) & ~(size_t)15;
 }
-__host__ inline size_t rt_lds_bytes(int E, int64_t T, int k) {
-  return rt_keys_off((size_t)rt_ksplit(E) * kRtTok * E * sizeof(float), rt_csr_bytes(E, T, k)) +
+__host__ inline size_t rt_lds_bytes(int E, int64_t T, int k, int P) {
+  const int En = rt_part_experts(E, P);   // the logits rows hold a part's experts
+  return rt_keys_off((size_t)rt_ksplit(En) * kRtTok * En * sizeof(float), rt_csr_bytes(E, T, k)) +
          (size_t)kRtWaves * kWave * sizeof(uint64_t);
 }
 // an upper bound of rt_lds_bytes over every accepted shape
@@ -179,11 +201,16 @@ __device__ __forceinline__ void csr_pad(const int* cnt, const int* base, int E, 
   for (int r = total + tid; r < mpad_max; r += nthreads) row_tok[r] = -1;
 }
 
-// The routing of tokens t0.. (at most 16) from their logits rows in LDS (part[tok][E]), then the
-// CSR by the workgroup that holds the last picks. counter: the caller's completion word when
-// several workgroups route (the one that completes the count builds the CSR from the ids in
-// memory), or NULL when this workgroup routes every token (the ids are in its LDS).
-// keys: 512 B of LDS per wavefront for the rank of an E <= 64 row (else unused).
+// The routing of tokens t0.. (at most 16) from their logits rows in LDS (part[tok][En], experts
+// e_lo..e_lo+En-1 of E), then the CSR by the workgroup that holds the last picks. counter: the
+// caller's completion word when several workgroups route (the one that completes the count
+// builds the CSR from the ids in memory), or NULL when this workgroup routes every token (the
+// ids are in its LDS). With an expert split (P = 2 parts, part `part` of group g), each
+// workgroup first takes the top k of its own experts, stores those candidates in the workspace
+// (cand) and counts itself in on its group's word (grp); the one that completes the pair merges
+// both parts' candidates under the same order (the top k of the union of each part's top k is
+// the top k of the row) and goes on alone; the other leaves.
+// keys: 512 B of LDS per wavefront for the ranks (E <= 64 rows, the merge).
 //
 // The CSR row of pick (t, s) routed to expert e is base[e] plus the number of earlier tokens
 // routed to e (a token picks an expert at most once). With several workgroups (groups of 16
@@ -192,43 +219,105 @@ __device__ __forceinline__ void csr_pad(const int* cnt, const int* base, int E, 
 // (device-scope stores, like the ids); the last workgroup histograms the picks per group in
 // LDS, scans the histograms over the groups, and places every pick at once. When the group
 // table does not fit, each wavefront of the last workgroup sweeps all ids for its experts.
-__device__ __forceinline__ void router_tail(float* part, int T, int t0, int E, int k, int tile_m,
-                                            int mpad_max, int32_t* __restrict__ ids,
-                                            float* __restrict__ w, int32_t* __restrict__ counts,
+__device__ __forceinline__ void router_tail(float* part, int T, int t0, int E, int En, int e_lo,
+                                            int k, int tile_m, int mpad_max,
+                                            int32_t* __restrict__ ids, float* __restrict__ w,
+                                            int32_t* __restrict__ counts,
                                             int32_t* __restrict__ basep,
                                             int32_t* __restrict__ row_tok,
                                             int32_t* __restrict__ pos, uint32_t* counter,
-                                            int n_groups, uint8_t* smem, uint64_t* keys) {
+                                            int n_groups, int P, int pidx, int g, uint32_t* grp,
+                                            uint32_t* cand, uint8_t* smem, uint64_t* keys) {
   __shared__ int s_last;
   __shared__ __attribute__((aligned(16))) int s_ids[kRtTok * MOE_MAX_K];   // this group's picks
+  __shared__ float s_pv[kRtTok * MOE_MAX_K];                                // their logits
   __shared__ int s_wave_tot[kRtWaves];
   const int tid = (int)threadIdx.x, nthreads = (int)blockDim.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), waves = nthreads >> 6;
+  const int ntok = min(kRtTok, T - t0);
 
-  // ---- top-k: wavefront w routes tokens t0 + w, t0 + w + waves, ... ----
-  for (int tt = wave; tt < kRtTok && t0 + tt < T; tt += waves) {
+  // ---- top-k of this workgroup's experts: wavefront w takes tokens t0 + w, t0 + w + waves, ...
+  for (int tt = wave; tt < ntok; tt += waves) {
     int my_id = 0;
     float my_v;
-    const float* row = part + (size_t)tt * E;
-    if (E <= kWave) {   // rank against the row's keys in LDS (row[lane] read for every lane)
-      const int rank = wave_rank_lds(row, keys + (size_t)wave * kWave, E);
+    const float* row = part + (size_t)tt * En;
+    if (En <= kWave) {   // rank against the row's keys in LDS (row[lane] read for every lane)
+      const int rank = wave_rank_lds(row, keys + (size_t)wave * kWave, En);
       for (int r = 0; r < k; ++r) {
         const int id = rank_pick(rank, r);
         if (lane == r) my_id = id;
       }
       my_v = row[min(max(my_id, 0), kWave - 1)];
     } else {
-      wave_topk(row, E, k, my_id, my_v);
+      wave_topk(row, En, k, my_id, my_v);
     }
-    // the ids are stored with device-scope atomic stores, which bypass the XCD's non-coherent
-    // L2, so that another XCD's workgroup can read them
+    if (lane < k) {
+      s_ids[tt * k + lane] = e_lo + my_id;
+      s_pv[tt * k + lane] = my_v;
+    }
+  }
+  __syncthreads();
+
+  if (P > 1) {
+    // this part's candidates into the workspace (device-scope stores), acknowledged, then the
+    // pair's count; the workgroup that completes it merges
+    uint32_t* const mine = cand + (size_t)(g * P + pidx) * kRtTok * k * 2;
+    for (int i = tid; i < ntok * k; i += nthreads) {
+      __hip_atomic_store(mine + 2 * i, __float_as_uint(s_pv[i]), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(mine + 2 * i + 1, (uint32_t)s_ids[i], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(grp + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)P - 1;
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0)   // ready for the next call
+      __hip_atomic_store(grp + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // merge: per token, lane j < P*k holds candidate j (part j / k, pick j % k), read with
+    // device-coherent loads; its rank among them by the same key gives the final picks
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(cand + (size_t)g * P * kRtTok * k * 2, (uint32_t)(P * kRtTok * k * 8));
+    const int n = P * k;
+    for (int tt = wave; tt < ntok; tt += waves) {
+      float cv = 0.0f;
+      int cid = 0;
+      uint64_t mk = 0;
+      if (lane < n) {
+        const int pp = lane / k, r = lane - pp * k;
+        const uint32_t off = (uint32_t)(((pp * kRtTok + tt) * k + r) * 8);
+        cv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, off, 0, 16));
+        cid = (int)__builtin_amdgcn_raw_buffer_load_b32(rc, off + 4, 0, 16);
+        mk = rank_key(cv, cid);
+      }
+      const int rank = wave_rank_keys(mk, keys + (size_t)wave * kWave, n);
+      for (int r = 0; r < k; ++r) {
+        const int src = rank_pick(rank, r);
+        const int id = __shfl(cid, src);
+        const float v = __shfl(cv, src);
+        if (lane == r) {
+          s_ids[tt * k + r] = id;
+          s_pv[tt * k + r] = v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- the picks: weights (softmax over the k picks), ids with device-scope atomic stores
+  // (they bypass the XCD's non-coherent L2, so that another XCD's workgroup can read them)
+  for (int tt = wave; tt < ntok; tt += waves) {
+    const int my_id = lane < k ? s_ids[tt * k + lane] : 0;
+    const float my_v = lane < k ? s_pv[tt * k + lane] : 0.0f;
     const float wt = topk_weight(my_v, k);
     if (lane < k) {
       __hip_atomic_store(ids + (size_t)(t0 + tt) * k + lane, my_id, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
       w[(size_t)(t0 + tt) * k + lane] = wt;
-      s_ids[tt * k + lane] = my_id;
     }
   }
   const int R = T * k;
@@ -261,7 +350,6 @@ __device__ __forceinline__ void router_tail(float* part, int T, int t0, int E, i
   const int G = n_groups;
   const bool grouped = rt_grouped(G, E);
   if (grouped) {
-    const int ntok = min(kRtTok, T - t0);
     for (int i = tid; i < ntok * k; i += nthreads) {
       const int e = s_ids[i], before = (i / k) * k;
       int lr = 0, j = 0;
@@ -451,55 +539,61 @@ __device__ __forceinline__ void router_tiles(__amdgpu_buffer_rsrc_t rw, __amdgpu
   }
 }
 
-// Workgroups of 16 wavefronts each take 16 tokens over the whole reduction.
+// Workgroups of 16 wavefronts each take 16 tokens over the whole reduction, and the experts of
+// one part (P parts; workgroup L: group L / P, part L % P).
 __global__ void __launch_bounds__(kRtThreads)
 router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
               const float* __restrict__ br, int T, int D, int E, int k, int tile_m,
               int mpad_max, float* __restrict__ logits, int32_t* __restrict__ ids,
               float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ basep,
               int32_t* __restrict__ row_tok, int32_t* __restrict__ pos,
-              uint32_t* __restrict__ ws) {
+              uint32_t* __restrict__ ws, int P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int t0 = (int)blockIdx.x * kRtTok;
-  const int ntiles = rt_tiles(E), ntg = rt_tgroups(E), ksplit = rt_ksplit(E);
+  const int g = (int)blockIdx.x / P, pidx = (int)blockIdx.x - g * P;
+  const int G = (int)gridDim.x / P;
+  const int t0 = g * kRtTok;
+  const int Ep = rt_part_experts(E, P), e_lo = pidx * Ep, En = min(Ep, E - e_lo);
+  const int ntiles = rt_tiles(En), ntg = rt_tgroups(En), ksplit = rt_ksplit(En);
   const int KS = D >> 5;   // 32-wide k steps
-  float* part = reinterpret_cast<float*>(smem);   // [ksplit][kRtTok][E]
+  float* part = reinterpret_cast<float*>(smem);   // [ksplit][kRtTok][En]
 
-  // ---- logits of the workgroup's 16 tokens: a wavefront per (tile group, K slice) ----
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wr, (uint32_t)E * D * 2);
+  // ---- logits of the workgroup's 16 tokens and En experts: a wavefront per (tile group, K
+  // slice) ----
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wr + (size_t)e_lo * D, (uint32_t)En * D * 2);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)T * D * 2);
   for (int u = wave; u < ntg * ksplit; u += kRtWaves) {
     const int tg = u % ntg, p = u / ntg;
     const int nt = min(kRtTpw, ntiles - tg * kRtTpw);
     f32x4_t acc[kRtTpw];
-    router_tiles(rw, rx, D, E, T, tg * kRtTpw * 16, nt, t0, p * KS / ksplit,
+    router_tiles(rw, rx, D, En, T, tg * kRtTpw * 16, nt, t0, p * KS / ksplit,
                  (p + 1) * KS / ksplit, acc);
 #pragma unroll
     for (int j = 0; j < kRtTpw; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = (tg * kRtTpw + j) * 16 + 4 * lg + i;
-        if (j < nt && e < E) part[((size_t)p * kRtTok + lr) * E + e] = acc[j][i];
+        if (j < nt && e < En) part[((size_t)p * kRtTok + lr) * En + e] = acc[j][i];
       }
   }
   __syncthreads();
-  for (int i = tid; i < kRtTok * E; i += kRtThreads) {
-    const int tok = i / E, e = i - tok * E;
-    float v = part[(size_t)tok * E + e];
-    for (int p = 1; p < ksplit; ++p) v += part[((size_t)p * kRtTok + tok) * E + e];
-    if (br) v += br[e];
-    part[(size_t)tok * E + e] = v;   // only this thread touches element (tok, e)
-    if (logits && t0 + tok < T) logits[(size_t)(t0 + tok) * E + e] = v;
+  for (int i = tid; i < kRtTok * En; i += kRtThreads) {
+    const int tok = i / En, e = i - tok * En;
+    float v = part[(size_t)tok * En + e];
+    for (int p = 1; p < ksplit; ++p) v += part[((size_t)p * kRtTok + tok) * En + e];
+    if (br) v += br[e_lo + e];
+    part[(size_t)tok * En + e] = v;   // only this thread touches element (tok, e)
+    if (logits && t0 + tok < T) logits[(size_t)(t0 + tok) * E + e_lo + e] = v;
   }
   __syncthreads();
   uint64_t* const keys = reinterpret_cast<uint64_t*>(
-      smem + rt_keys_off((size_t)ksplit * kRtTok * E * sizeof(float), rt_csr_bytes(E, T, k)));
-  router_tail(part, T, t0, E, k, tile_m, mpad_max, ids, w, counts, basep, row_tok, pos,
-              gridDim.x == 1 ? nullptr : ws, (int)gridDim.x, smem, keys);
+      smem + rt_keys_off((size_t)ksplit * kRtTok * En * sizeof(float), rt_csr_bytes(E, T, k)));
+  router_tail(part, T, t0, E, En, e_lo, k, tile_m, mpad_max, ids, w, counts, basep, row_tok, pos,
+              gridDim.x == 1 ? nullptr : ws, G, P, pidx, g, ws + kRtGrpOff, ws + kRtDataOff, smem,
+              keys);
 }
 
 // A few tokens (T <= 16, E <= 256): the reduction split over `nsplit` small workgroups, so that
@@ -523,7 +617,7 @@ router_split_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
   const int lr = lane & 15, lg = lane >> 4;
   const int s = (int)blockIdx.x;
   const int KS = D >> 5;
-  float* const partg = reinterpret_cast<float*>(ws + kRtPartOff);   // [nsplit][T][E]
+  float* const partg = reinterpret_cast<float*>(ws + kRtDataOff);   // [nsplit][T][E]
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wr, (uint32_t)E * D * 2);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)T * D * 2);
   for (int tile = wave; tile < rt_tiles(E); tile += kSpWaves) {
@@ -571,8 +665,8 @@ router_split_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
   __syncthreads();
   uint64_t* const keys = reinterpret_cast<uint64_t*>(
       smem + rt_keys_off((size_t)kRtTok * E * sizeof(float), (size_t)(2 * E + T * k) * sizeof(int)));
-  router_tail(part, T, 0, E, k, tile_m, mpad_max, ids, w, counts, basep, row_tok, pos, nullptr,
-              1, smem, keys);
+  router_tail(part, T, 0, E, E, 0, k, tile_m, mpad_max, ids, w, counts, basep, row_tok, pos,
+              nullptr, 1, 1, 0, 0, nullptr, nullptr, smem, keys);
 }
 
 }  // namespace moe
@@ -596,7 +690,7 @@ extern "C" int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b
   const int KS = D / 32;
   int nsplit = 0;
   if (T <= moe::kRtTok && E <= moe::kSpThreads) {
-    const int64_t cap = (MOE_ROUTER_WS_WORDS - moe::kRtPartOff) / (T * (int64_t)E);
+    const int64_t cap = (MOE_ROUTER_WS_WORDS - moe::kRtDataOff) / (T * (int64_t)E);
     nsplit = (int)std::min<int64_t>(std::min<int64_t>(cap, KS), moe::kSpMaxSplit);
   }
   if (nsplit >= 2) {
@@ -606,9 +700,19 @@ extern "C" int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b
                 nsplit);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
   }
-  const size_t lds = moe::rt_lds_bytes(E, T, k);
-  static bool lds_attr_set[moe::kMaxDevices] = {};   // > 64 KB of LDS: opt in once per device
+  static int cus_of[moe::kMaxDevices] = {};
   const int dslot = moe::device_slot();
+  int cus = dslot >= 0 ? cus_of[dslot] : 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MOE_ELAUNCH;
+    if (dslot >= 0) cus_of[dslot] = cus;
+  }
+  const int P = moe::rt_parts(T, E, cus);
+  const size_t lds = moe::rt_lds_bytes(E, T, k, P);
+  static bool lds_attr_set[moe::kMaxDevices] = {};   // > 64 KB of LDS: opt in once per device
   if (dslot < 0 || !lds_attr_set[dslot]) {
     const size_t most = moe::rt_lds_most();
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&moe::router_kernel),
@@ -616,9 +720,9 @@ extern "C" int moe_router(const uint16_t* x, const uint16_t* w_r, const float* b
       return MOE_ELAUNCH;
     if (dslot >= 0) lds_attr_set[dslot] = true;
   }
-  const int64_t blocks = (T + moe::kRtTok - 1) / moe::kRtTok;
+  const int64_t blocks = (T + moe::kRtTok - 1) / moe::kRtTok * P;
   moe::launch(moe::router_kernel, dim3((unsigned)blocks), dim3(moe::kRtThreads), (unsigned)lds,
               (hipStream_t)stream, x, w_r, b_r, (int)T, D, E, k, tile_m, (int)mpad_max, logits,
-              ids, w, counts, basep, row_tok, pos, ws);
+              ids, w, counts, basep, row_tok, pos, ws, P);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

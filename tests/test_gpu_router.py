@@ -5,9 +5,11 @@ Protocol: the fp32 logits within |gpu - ref| <= 1e-3 * S + 1e-5 of oracle.router
 routing decisions taken on the GPU's own fp32 logits (ids, weights) and the CSR built from the
 GPU's ids equal the oracle's route_topk and bucket bit for bit; the workspace's counter word is
 left zero. A few tokens (T <= 16, E <= 256) take the split-reduction kernel, more the
-one-workgroup-per-16-tokens kernel, whose last workgroup builds the CSR from per-group
-histograms (or, when their table does not fit its LDS, by sweeping all ids per expert); each is
-covered, and one workspace serves both kernels in turn.
+one-workgroup-per-16-tokens kernel (for E >= 64 a pair of workgroups per 16 tokens, each with
+half of the experts, whose top-k candidates the later one merges), whose last workgroup builds
+the CSR from per-group histograms (or, when their table does not fit its LDS, by sweeping all ids
+per expert); each is covered, and one workspace serves both kernels in turn. Every counter word
+of the workspace is left zero.
 """
 import numpy as np
 import pytest
@@ -52,7 +54,9 @@ def check_router(x, w, b, k, tile_m, want_logits=True, ws=None):
     out = moe.moe_router(bf16_dev(x), bf16_dev(w), None if b is None else dev(b), k, tile_m, ws,
                          want_logits=True)
     torch.cuda.synchronize()
-    assert int(host(ws)[0]) == 0, "counter word not left zero"
+    wsh = host(ws)
+    assert int(wsh[0]) == 0, "counter word not left zero"
+    assert int(abs(wsh[64:1088]).max()) == 0, "pair counters not left zero"
     lg = host(out["logits"])
     ref, S = oracle.router_logits(x, w, b)
     assert_within(lg, ref, S, "router logits")
