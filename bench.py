@@ -574,9 +574,9 @@ def _time_decode_layers(oracle, synth, wl, budget_s):
 
 
 def _time_prefill_sample(oracle, synth, wl, n_experts):
-    """The oracle's two projections of a pp512 layer on the first n_experts live experts (their
-    routed rows), plus route + bucket of the whole layer; returns (seconds for the sample, the
-    sample's flops, the layer's flops)."""
+    """The oracle's two projections of a prefill layer on the first n_experts live experts (their
+    routed rows), plus route + bucket of the whole layer; returns (seconds of route + bucket,
+    seconds of the sample's projections, the sample's routed rows)."""
     tok = synth.tokens(wl, 0)
     W = synth.layer_weights(wl, 0)
     t0 = time.perf_counter()
@@ -602,8 +602,8 @@ def _time_prefill_sample(oracle, synth, wl, n_experts):
 
 
 def cpu_baseline(synth, budget_s):
-    """The CPU oracle (as it stands) on bounded samples of the decode and pp512 workloads, on one
-    host thread and on all of them (numpy's BLAS threads)."""
+    """The CPU oracle (as it stands) on bounded samples: the decode workload on one host thread
+    and on all of them (numpy's BLAS threads), the pp512 and 120b prefill layers on all."""
     import oracle
     from threadpoolctl import threadpool_limits
     wl = synth.WORKLOADS["decode_t1"]
@@ -612,12 +612,20 @@ def cpu_baseline(synth, budget_s):
         t1, n1 = _time_decode_layers(oracle, synth, wl, budget_s)
     with threadpool_limits(limits=cores):
         ta, na = _time_decode_layers(oracle, synth, wl, budget_s)
-    pw = synth.WORKLOADS["prefill_pp512"]
-    with threadpool_limits(limits=cores):
-        tf, tp, n_rows = _time_prefill_sample(oracle, synth, pw, 4)
-    R = pw.T * pw.k
-    layer_s = tf + tp * R / n_rows               # the projections scale with the routed rows
-    gflops = chain_flops(pw) * n_rows / R / tp / 1e9
+    prefill = {}
+    for name in ("prefill_pp512", "prefill_120b_t2048"):   # all host threads only
+        pw = synth.WORKLOADS[name]
+        with threadpool_limits(limits=cores):
+            tf, tp, n_rows = _time_prefill_sample(oracle, synth, pw, 4)
+        R = pw.T * pw.k
+        layer_s = tf + tp * R / n_rows               # the projections scale with the routed rows
+        gflops = chain_flops(pw) * n_rows / R / tp / 1e9
+        prefill[name] = {"tokens_per_s": round(pw.T / layer_s, 2),
+                         "s_per_layer": round(layer_s, 2), "GFLOPs": round(gflops, 2),
+                         "cores": cores,
+                         "sample": f"route + bucket of layer 0 ({tf:.2f} s) and the two "
+                                   f"projections of its first 4 live experts ({n_rows} routed "
+                                   f"rows, {tp:.2f} s), scaled to the layer's {R} rows"}
     return {"value": round(wl.T / (ta * wl.layers), 4), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": f"oracle.chain (float64 numpy, {cores} threads) on 1 token through layers "
@@ -626,13 +634,7 @@ def cpu_baseline(synth, budget_s):
             "single_thread": {"value": round(wl.T / (t1 * wl.layers), 4), "unit": "tokens/s",
                               "cores": 1, "ms_per_layer": round(t1 * 1e3, 1),
                               "sample": f"layers 0..{n1 - 1}"},
-            "prefill_pp512": {"tokens_per_s": round(pw.T / layer_s, 2),
-                              "s_per_layer": round(layer_s, 2), "GFLOPs": round(gflops, 2),
-                              "cores": cores,
-                              "sample": f"route + bucket of layer 0 ({tf:.2f} s) and the two "
-                                        f"projections of its first 4 live experts ({n_rows} routed "
-                                        f"rows, {tp:.2f} s), scaled to the layer's {R} rows"},
-            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+            **prefill, "nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 # ------------------------------------------------------------------------------------------
