@@ -5,18 +5,24 @@
 // it, so no separate serial prefix pass (and no extra dispatch or barrier level) is needed; the
 // CSR it produces is the same bit for bit. Here every workgroup histograms all T*k ids in LDS,
 // sums the padded counts of the experts below its own to get basep[e], then compacts its rows in
-// ascending token order with wavefront ballots (an ordered scan, so the result is unique).
+// ascending token order with wavefront ballots (an ordered scan, so the result is unique). The
+// ids are read kBucketUnroll loads at a time per thread (all in flight before the histogram's
+// atomics) and, when T*k fits kBucketStaged ids, kept in LDS for the compaction, which then
+// reads no memory.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
 constexpr int kBucketThreads = 256;
+constexpr int kBucketUnroll = 8;          // id loads in flight per thread
+constexpr int kBucketStaged = 12 * 1024;  // ids kept in LDS for the compaction (48 KB), at most
 
 __global__ void __launch_bounds__(kBucketThreads)
 bucket_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int E, int tile_m,
               int64_t mpad_max, int32_t* __restrict__ counts, int32_t* __restrict__ basep,
-              int32_t* __restrict__ row_tok, int32_t* __restrict__ pos) {
+              int32_t* __restrict__ row_tok, int32_t* __restrict__ pos, int staged) {
+  extern __shared__ int idl[];   // [T*k] when staged
   __shared__ int hist[MOE_MAX_E];
   __shared__ int red[kBucketThreads / kWave][2];
   __shared__ int wave_tot[kBucketThreads / kWave];
@@ -27,9 +33,19 @@ bucket_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int E, int tile
 
   for (int i = tid; i < E; i += kBucketThreads) hist[i] = 0;
   __syncthreads();
-  for (int64_t i = tid; i < R; i += kBucketThreads) {
-    const int id = ids[i];
-    if ((unsigned)id < (unsigned)E) atomicAdd(&hist[id], 1);  // ids outside [0,E) are ignored
+  for (int64_t i0 = 0; i0 < R; i0 += (int64_t)kBucketThreads * kBucketUnroll) {
+    int v[kBucketUnroll];
+#pragma unroll
+    for (int u = 0; u < kBucketUnroll; ++u) {
+      const int64_t i = i0 + u * kBucketThreads + tid;
+      v[u] = i < R ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBucketUnroll; ++u) {
+      const int64_t i = i0 + u * kBucketThreads + tid;
+      if (staged && i < R) idl[i] = v[u];
+      if ((unsigned)v[u] < (unsigned)E) atomicAdd(&hist[v[u]], 1);  // ids outside [0,E): ignored
+    }
   }
   __syncthreads();
 
@@ -67,7 +83,7 @@ bucket_kernel(const int32_t* __restrict__ ids, int64_t T, int k, int E, int tile
     int slot = -1;
     if (t < T)
       for (int s = 0; s < k; ++s)
-        if (ids[t * k + s] == e) slot = s;
+        if ((staged ? idl[t * k + s] : ids[t * k + s]) == e) slot = s;
     const uint64_t ballot = __ballot(slot >= 0);
     const int in_wave = __popcll(ballot & (lane ? (~0ull >> (64 - lane)) : 0ull));
     if (lane == 0) wave_tot[wave] = __popcll(ballot);
@@ -108,8 +124,10 @@ extern "C" int moe_bucket(const int32_t* ids, int64_t T, int k, int E, int tile_
   if (E > MOE_MAX_E || tile_m < 1 || tile_m > MOE_MAX_TILE_M) return MOE_ESHAPE;
   const int64_t need = moe_mpad_max(T, k, E, tile_m);
   if (mpad_max < need || mpad_max > 0x7FFFFFFFLL) return MOE_ESHAPE;
-  moe::launch(moe::bucket_kernel, dim3((unsigned)E), dim3(moe::kBucketThreads), 0,
-                     (hipStream_t)stream, ids, T, k, E, tile_m, mpad_max, counts, basep, row_tok,
-                     pos);
+  const int64_t R = T * (int64_t)k;
+  const int staged = R <= moe::kBucketStaged ? 1 : 0;
+  moe::launch(moe::bucket_kernel, dim3((unsigned)E), dim3(moe::kBucketThreads),
+              staged ? (size_t)R * sizeof(int) : 0, (hipStream_t)stream, ids, T, k, E, tile_m,
+              mpad_max, counts, basep, row_tok, pos, staged);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

@@ -120,7 +120,10 @@ def test_route_and_bucket_bit_exact(name):
 @pytest.mark.parametrize("T,k,E,tile_m,skew", [(1, 4, 32, 1, 0.0), (1, 4, 32, 16, 0.0),
                                                (300, 1, 4, 16, 0.0), (777, 8, 64, 7, 2.0),
                                                (64, 4, 32, 32, 4.0), (5, 5, 5, 256, 0.0),
-                                               (1000, 4, 1024, 16, 0.0)])
+                                               (1000, 4, 1024, 16, 0.0),
+                                               # T*k past the ids the kernel keeps in LDS, and
+                                               # exactly at that limit
+                                               (4000, 4, 64, 16, 1.0), (3072, 4, 128, 16, 0.0)])
 def test_bucket_edge_shapes_bit_exact(T, k, E, tile_m, skew):
     ids = synth.random_ids(T + E, T, k, E, skew=skew)
     log(f"bucket T={T} k={k} E={E} tile_m={tile_m}")
