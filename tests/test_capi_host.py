@@ -285,3 +285,25 @@ def test_library_binds_to_torchs_hip_runtime():
             "assert os.path.realpath(maps.pop()).startswith(tdir + os.sep)\n") % root
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_binding_constants_match_the_header():
+    """The binding's copies of the header's sizes and limits (workspace sizes, maxima, status and
+    activation codes) are the header's values: a caller that sizes a workspace from the binding
+    gets what the library expects."""
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "include", "moe_mx4.h")).read()
+    defines = {m.group(1): int(m.group(2))
+               for m in re.finditer(r"^#define (MOE_[A-Z0-9_]+) (\d+)", hdr, re.M)}
+    enums = {m.group(1): int(m.group(2))
+             for m in re.finditer(r"^\s+(MOE_[A-Z0-9_]+) = (\d+)", hdr, re.M)}
+    seen = 0
+    for name, value in {**defines, **enums}.items():
+        if hasattr(_lib, name):
+            assert getattr(_lib, name) == value, name
+            seen += 1
+    for name in ("MOE_ROUTER_WS_WORDS", "MOE_DECODE_WS_WORDS", "MOE_ROUTER_MAX_ROUTED",
+                 "MOE_MAX_E", "MOE_MAX_K", "MOE_OK", "MOE_ELAUNCH", "MOE_ACT_SWIGLU_OAI"):
+        assert name in defines or name in enums, name
+        assert hasattr(_lib, name), name
+    assert seen >= 12
