@@ -37,9 +37,9 @@
 //    publishes the activation chunk to all wavefronts and frees the LDS buffer (of 4) that the
 //    iteration's DMA overwrites.
 //  * Activation rows are gathered through a_row (row_tok) by the DMA, 128 k (256 B) per row
-//    per chunk, into an XOR-swizzled LDS layout (16-byte piece q of row m at slot q ^ (m % 16)),
-//    so the B-fragment reads of 16 consecutive rows hit 16 different bank groups; every B
-//    fragment feeds 4 MFMAs (the wavefront's 4 weight tiles).
+//    per chunk, into an XOR-swizzled LDS layout (16-byte piece q of row m at slot
+//    q ^ gemm_swz16(m)), so the 1 KB B-fragment reads of 16 consecutive rows run at the LDS's
+//    full rate; every B fragment feeds the wavefront's 2 (SwiGLU) or 3 weight tiles.
 //  * Accumulators start at the bias of their weight row. Token tiles past the expert's count are
 //    never computed; rows past the count are never stored. Experts with no rows exit at once.
 //  * SwiGLU mode pairs gate tiles with the matching up tiles in the same wavefront, so the
@@ -102,6 +102,12 @@ __host__ __device__ constexpr int gemm_lds_bytes(bool mx8) {
 // 128 bytes: the B-fragment reads of 16 consecutive rows at one q then touch 16 different
 // 16-byte bank groups (8 different ones for rows m and m + 8 apart in the low bit)
 __device__ __forceinline__ int gemm_swz8(int m) { return (m & 7) ^ ((m >> 3) & 1); }
+// 16-byte piece q of routed row m of a bf16 chunk (256 bytes) sits at slot q ^ gemm_swz16(m):
+// m % 16 rotated left by one bit. Measured with the LDS counters on gfx950 (one ds_read_b128
+// per lane, lane (r, g) reading piece 4g + i of row r, rows 256 bytes apart): this mask costs the
+// 4 LDS cycles of a contiguous 1 KB read, while the plain mask m % 16 costs 8, half of them
+// bank-conflict stalls.
+__device__ __forceinline__ int gemm_swz16(int m) { return ((m << 1) & 14) | ((m >> 3) & 1); }
 
 // Everything one pass over up to 16*NTT routed rows of one expert needs.
 struct GemmCtx {
@@ -312,13 +318,13 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
 
   // activation DMA: instruction i of this wavefront covers 16-byte slots p = j*64 + lane,
   // j = wave + 8*i, i.e. routed row m = p / 16 of the pass and swizzled slot p % 16, which
-  // holds the row's piece q = (p % 16) ^ (m % 16) of the chunk
+  // holds the row's piece q = (p % 16) ^ gemm_swz16(m) of the chunk
   uint32_t xo[NX], xol[NX];
 #pragma unroll
   for (int i = 0; i < NX; ++i) {
     const int p = (wave + kGmWaves * i) * 64 + lane;
     const int m = p / PIECES;
-    const int q = (p % PIECES) ^ (m & 15);
+    const int q = (p % PIECES) ^ gemm_swz16(m);
     const bool ok = m < g.live && wave + kGmWaves * i < KBS;
     const uint32_t src = gemm_src_row(g, m, ok);
     const uint32_t off = ok ? src * (uint32_t)g.K * 2 + q * 16 : kOOB;
@@ -382,7 +388,7 @@ __device__ __forceinline__ void gemm_pass(const GemmCtx& g, uint8_t* __restrict_
     }
   }
 
-  const int swz = lr;   // m % 16 == lr for every token tile
+  const int swz = gemm_swz16(lr);   // m % 16 == lr for every token tile
   // a do-while: C >= 1, and a loop the compiler may skip lets it sink the prologue's weight
   // loads into the loop's entry block, below the DMA copies
   int c0 = 0;
