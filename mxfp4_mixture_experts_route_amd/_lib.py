@@ -11,7 +11,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe_mx4.so")
+# the in-tree build; MOE_MX4_LIB names another build of the same sources (e.g. a sanitized one)
+LIB_PATH = os.environ.get("MOE_MX4_LIB") or os.path.join(PKG, "libmoe_mx4.so")
 
 MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EALIGN, MOE_ELAUNCH = 0, 1, 2, 3, 4
 MOE_ACT_NONE, MOE_ACT_SWIGLU_OAI, MOE_ACT_SWIGLU_OAI_MX8 = 0, 1, 2

@@ -38,8 +38,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra: list[str], build_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc()] + CFLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -47,20 +47,24 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+def build(verbose: bool = False, extra: list[str] | None = None, out_path: str = LIB_PATH,
+          build_dir: str = BUILD_DIR, link_extra: list[str] | None = None) -> str:
+    """Compile every source with CFLAGS + extra into build_dir and link out_path (by default
+    the in-tree library the package loads)."""
     extra = list(extra or [])
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), SOURCES))
+    tmp = out_path + ".tmp"
+    cmd = ([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"] + list(link_extra or []) +
+           ["-o", tmp] + objs)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out_path)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {out_path}")
+    return out_path
 
 
 if __name__ == "__main__":
